@@ -1,0 +1,209 @@
+/*
+ * moe.h -- C ABI of libmoe.so, the routed-expert mixture-of-experts layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (one DeepSeek-V4-class MoE layer, routed experts only):
+ *
+ *   z[t,e]  = x[t] . Wr[e] + bias[e]                      router logits
+ *   ids[t]  = the k experts with the largest z, ties to the lower expert index
+ *   w[t,j]  = sigmoid(z[t,ids[t,j]]) / sum_j' sigmoid(z[t,ids[t,j']])
+ *   y[t,j]  = D_e (silu(G_e x[t]) * (U_e x[t])),  e = ids[t,j]
+ *   out[t]  = sum_{j = 0..k-1, ids[t,j] owned} w[t,j] * y[t,j]
+ *
+ * The pages this layer comes from:
+ *  - aeonmindai/arc PR #89, "Stage 1 -- EP=2": experts are split into shares,
+ *    global ids are remapped to share-local ids through device tables built
+ *    once at load, unowned slots are masked, and a share's partial is the sum
+ *    over the slots it owns, so the partials over any partition add up to the
+ *    full output.  The same section: placements are contiguous, explicit or
+ *    LPT-balanced; the expert axis is sliced at load and unsupported formats
+ *    are refused by name; a size that disagrees with the placement is an
+ *    error, never a silent fallback.
+ *  - arc PR #89, "Stage 0": pointers are checked against the device ordinal,
+ *    not only the device kind; the per-share load counter is a device-side
+ *    array read back outside any captured region.
+ *  - TrevorS/ds4 PR #13, "Tested": accumulating the routed down projection
+ *    with float atomics makes runs drift; here every reduction has a fixed
+ *    order and the library uses no floating-point atomics, so repeated calls
+ *    give bit-identical results.
+ *  - antirez/ds4 PR #754, "Supported paths and safety": 2-bit routed gate/up
+ *    and down projections, Q8_0 dense projections (here: the router, and the
+ *    routed down projection of the batched workloads).
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are caller-allocated HIP device memory on the device of
+ *    the stream `s` (NULL stream = the current device).  The library
+ *    allocates nothing and keeps no pointer after a call returns.
+ *  - Calls are asynchronous on `s`; they never synchronise and never copy to
+ *    the host, so they may be captured in a HIP graph.  Results are visible
+ *    after the stream is synchronised.
+ *  - All arguments are checked before anything is launched.  On an error the
+ *    call returns a non-zero moe_status, launches nothing, leaves every output
+ *    unmodified, and moe_last_error() describes the problem (thread-local).
+ *  - T = 0 is a successful no-op.  There are no environment switches and no
+ *    fallback paths: the activation dtype selects the kernels (fp32: dequant
+ *    GEMV family; bf16: grouped MFMA GEMM).
+ *  - Calls that overlap on one stream are ordered; calls sharing a workspace
+ *    on different streams race.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,          /* bad size, null pointer, k > E, inconsistent shapes */
+  MOE_ERR_UNSUPPORTED = 2,  /* format / size outside what the kernels implement */
+  MOE_ERR_DEVICE = 3,       /* a pointer is not device memory of the stream's device */
+  MOE_ERR_WORKSPACE = 4,    /* workspace missing or smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 5           /* a HIP runtime call failed (launch, attribute query) */
+} moe_status;
+
+/* Weight formats.  Blocks of 32 values run along the contraction axis.
+ *   MOE_W_F32  : plain fp32.
+ *   MOE_W_Q8_0 : 32 int8 codes q and one fp16 scale d; value = d*q.
+ *   MOE_W_Q2SM : 32 two-bit codes q in {0..3}, fp16 scale d and fp16 min m;
+ *                value = d*q + m.  A stand-in for the pages' 2-bit routed
+ *                formats (IQ2_XXS / Q2_K), whose codebooks are not given. */
+typedef enum { MOE_W_F32 = 0, MOE_W_Q8_0 = 1, MOE_W_Q2SM = 2 } moe_wfmt;
+
+typedef enum { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 } moe_act;
+
+/* A stack of n matrices, each `rows` outputs x `cols` inputs, in the planar
+ * device layout written by moe_pack_planar():
+ *   F32  : codes = float  [n][rows][cols];                    scales = NULL
+ *   Q8_0 : codes = int8   [n][rows][cols];                    scales = fp16 d      [n][rows][cols/32]
+ *   Q2SM : codes = uint8  [n][rows][cols/4]  (value i of a row in byte i/4,
+ *          bits 2*(i%4)..+1);                                  scales = fp16 {d,m}  [n][rows][cols/32][2]
+ * cols must be a multiple of 32. */
+typedef struct {
+  int32_t fmt;
+  int32_t rows;
+  int32_t cols;
+  const void* codes;
+  const void* scales;
+} moe_qmat;
+
+/* The experts a caller owns, indexed by LOCAL id 0..n_experts-1.
+ * gate, up: rows = I, cols = H.  down: rows = H, cols = I. */
+typedef struct {
+  moe_qmat gate;
+  moe_qmat up;
+  moe_qmat down;
+  int32_t n_experts;
+} moe_experts;
+
+/* Message describing the last error on the calling thread ("" after success). */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+/* Bytes of workspace each call needs for the given shapes.  Any output may be
+ * NULL.  xt selects the expert kernels (their workspace differs).  */
+moe_status moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t k, int32_t E, int32_t E_local,
+                              int32_t xt, size_t* route_ws, size_t* group_ws, size_t* forward_ws);
+
+/* Router scoring and top-k selection (one token per row of x).
+ *   x      : [T, H] fp32 or bf16 (xt), row-major.
+ *   router : rows = E, cols = H, n = 1; format F32 or Q8_0.
+ *   bias   : [E] fp32 added to every logit (used for selection and weights), or NULL.
+ *   ids    : [T, k] int32 out, experts by decreasing logit, ties to the lower index.
+ *   w      : [T, k] fp32 out, sigmoid scores of the selected experts renormalised to sum 1.
+ * Logits are computed in one fixed fp32 order (per 32-block a chain of fused
+ * multiply-adds from 0, times the block scale, then a balanced pairwise sum
+ * over blocks, then + bias), so ids are reproducible bit for bit and equal to
+ * any implementation of that order.  Weights are evaluated in fp64 and rounded.
+ * Limits: 1 <= k <= min(E, 32), E <= 1024, H <= 16384.  */
+moe_status moe_route(const void* x, int32_t xt, int32_t T, int32_t H, const moe_qmat* router,
+                     const float* bias, int32_t k, int32_t* ids, float* w, void* ws, size_t ws_bytes,
+                     hipStream_t s);
+
+/* Group the T*k routing slots (slot s = t*k + j) by expert.
+ *   counts    : [E] int32 out, slots routed to each expert (the per-expert token
+ *               load; the number of non-zero entries is the count of distinct
+ *               experts the batch touches).
+ *   offsets   : [E+1] int32 out, exclusive prefix sum of counts.
+ *   slot_list : [T*k] int32 out, slots of expert e at offsets[e]..offsets[e+1]-1,
+ *               in ascending slot order (a stable sort; bit-reproducible).
+ * ids outside [0, E) are left out of the grouping.  Limits: E <= 1024. */
+moe_status moe_group_tokens(const int32_t* ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
+                            int32_t* offsets, int32_t* slot_list, void* ws, size_t ws_bytes,
+                            hipStream_t s);
+
+/* The owned experts' FFN for every routed slot they own.
+ *   x       : [T, H] fp32 or bf16 (xt), the same tensor given to moe_route.
+ *   local   : the owned expert stack, local-indexed (gate/up Q8_0 or Q2SM,
+ *             down Q8_0 or Q2SM; F32 expert weights are not supported).
+ *   g2l     : [E] int32 device table, global id -> local id, -1 = unowned (the
+ *             owned-expert mask); NULL = every expert owned with local = global.
+ *   counts, offsets, slot_list : from moe_group_tokens.
+ *   y_slot  : [T*k, H] fp32 out; row s = D_e(silu(G_e x) * U_e x) for owned
+ *             slots, rows of unowned slots are left untouched.
+ * E_local must equal local->n_experts; the table's consistency is checked once
+ * on the host with moe_plan_check().  fp32 activations run the dequant-GEMV
+ * kernels; bf16 activations run the grouped MFMA GEMM, whose intermediate
+ * silu(g)*u keeps fp32 precision (a bf16 hi/lo pair).
+ * Limits: H and I multiples of 32, H <= 8192, I <= 8192. */
+moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, int32_t I, int32_t k,
+                              const moe_experts* local, const int32_t* g2l, int32_t E, int32_t E_local,
+                              const int32_t* counts, const int32_t* offsets, const int32_t* slot_list,
+                              float* y_slot, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Weighted combine: out[t] = sum over j = 0..k-1 in that order, of owned slots,
+ * of w[t,j] * y_slot[t*k+j], starting from +0.0, in fp32, with no atomics.
+ * g2l NULL = every slot owned.  out: [T, H] fp32. */
+moe_status moe_combine(const float* y_slot, const float* w, const int32_t* ids, const int32_t* g2l,
+                       int32_t T, int32_t k, int32_t H, int32_t E, float* out, hipStream_t s);
+
+/* ---- profiling ------------------------------------------------------------ */
+
+/* Record HIP events around launches of one kernel, for live per-kernel timing.
+ * While set (on the calling thread), the i-th launch of the kernel called
+ * `name` gets hipEventRecord(start[i]) before and hipEventRecord(stop[i])
+ * after it on the call's stream, for i < n; *count holds how many launches
+ * were recorded.  Kernel names: route_logits, route_topk, group, active,
+ * gemv_gateup, gemv_down, combine.  The caller owns the events and must keep
+ * them, and count, alive while tracing; n <= 0 switches tracing off. */
+moe_status moe_trace_kernel(const char* name, hipEvent_t* start, hipEvent_t* stop, int32_t n, int32_t* count);
+
+/* ---- host helpers (no device access) ---------------------------------- */
+
+/* Sizes of the planar code and scale planes for one rows x cols matrix. */
+moe_status moe_planar_bytes(int32_t fmt, int32_t rows, int32_t cols, size_t* codes_bytes,
+                            size_t* scales_bytes);
+
+/* Re-lay n matrices from the definition layout (array of blocks: Q8_0
+ * {fp16 d; int8 q[32]}, Q2SM {fp16 d; fp16 m; uint8 qs[8]}, F32 plain rows)
+ * into the planar layout above.  Host memory in and out; a byte permutation. */
+moe_status moe_pack_planar(int32_t fmt, int32_t n, int32_t rows, int32_t cols, const void* aos,
+                           void* codes, void* scales);
+
+/* LPT-balanced placement of E experts onto n_shares shares of E/n_shares
+ * experts each (arc PR #89, "Stage 1"): experts by load descending (ties to
+ * the lower id), each to the least-loaded share with room (ties to the lower
+ * share).  owner: [E] out. */
+moe_status moe_place_lpt(const int64_t* load, int32_t E, int32_t n_shares, int32_t* owner);
+
+/* Tables of one share: g2l [E] (-1 = unowned) and l2g [E] (first *E_local
+ * entries used).  Local ids ascend with global id, or with local_order[e]
+ * when local_order is not NULL (a permuted placement). */
+moe_status moe_share_tables(const int32_t* owner, int32_t E, int32_t share, const int32_t* local_order,
+                            int32_t* g2l, int32_t* l2g, int32_t* E_local);
+
+/* Check a global->local table once at load: every entry is -1 or a local id,
+ * the owned ids are a bijection onto 0..E_local-1. */
+moe_status moe_plan_check(const int32_t* g2l, int32_t E, int32_t E_local);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -169,6 +169,7 @@ void oracle_route(const float* x, int T, int H, int E, int router_fmt, const uin
  * (slots of one expert in ascending s). */
 void oracle_group(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
                   int32_t* slot_list) {
+  if (E <= 0) return;
   int64_t n = (int64_t)T * k;
   for (int e = 0; e < E; ++e) counts[e] = 0;
   for (int64_t s = 0; s < n; ++s) counts[ids[s]]++;

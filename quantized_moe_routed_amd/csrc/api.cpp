@@ -1,0 +1,439 @@
+// The C ABI of libmoe: argument checks, workspace layout and kernel dispatch.
+// Every check runs before the first launch; a failing call launches nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "device.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+constexpr int kMaxRouteH = 16384;
+constexpr int kMaxFfnDim = 8192;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Device of a stream (NULL stream: the current device).
+moe_status stream_device(hipStream_t s, int* dev) {
+  hipError_t e = s ? hipStreamGetDevice(s, dev) : hipGetDevice(dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MOE_ERR_HIP, "cannot query the stream's device: %s", hipGetErrorString(e));
+  }
+  return MOE_OK;
+}
+
+// The pointer must be device (or managed) memory of device `dev` (the ordinal,
+// not only the kind: arc PR #89, Stage 0).
+moe_status check_dev(const void* p, int dev, const char* name) {
+  if (!p) return MOE_OK;
+  hipPointerAttribute_t a;
+  hipError_t e = hipPointerGetAttributes(&a, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MOE_ERR_DEVICE, "%s is not HIP device memory", name);
+  }
+  if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged)
+    return fail(MOE_ERR_DEVICE, "%s is not device memory (memory type %d)", name, (int)a.type);
+  if (a.device != dev)
+    return fail(MOE_ERR_DEVICE, "%s lives on device %d but the stream runs on device %d", name, a.device, dev);
+  return MOE_OK;
+}
+
+struct DevCheck {
+  int dev = 0;
+  moe_status st = MOE_OK;
+  void operator()(const void* p, const char* name) {
+    if (st == MOE_OK) st = check_dev(p, dev, name);
+  }
+};
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  (void)hipGetLastError();
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- kernel event tracing (thread-local; off unless moe_trace_kernel set it) ----
+struct Trace {
+  std::string name;
+  hipEvent_t* start = nullptr;
+  hipEvent_t* stop = nullptr;
+  int n = 0;
+  int32_t* count = nullptr;
+};
+thread_local Trace g_trace;
+
+moe::QMat qm(const moe_qmat& m) { return moe::QMat{m.codes, m.scales, m.rows, m.cols}; }
+
+// ---- workspace layouts -------------------------------------------------------
+size_t route_ws_bytes(int T, int E) { return align_up((size_t)T * E * sizeof(float)); }
+
+struct FwdLayout {
+  size_t n_act, act, h, total;
+};
+
+FwdLayout fwd_layout(int T, int I, int k, int E, int xt) {
+  (void)xt;
+  FwdLayout L;
+  size_t off = 0;
+  L.n_act = off;
+  off += kAlign;
+  L.act = off;
+  off += align_up((size_t)E * sizeof(int32_t));
+  L.h = off;
+  off += align_up((size_t)T * k * I * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+moe_status check_qmat(const moe_qmat& m, const char* name, int rows, int cols, bool allow_q2sm, bool allow_f32) {
+  if (m.fmt != MOE_W_F32 && m.fmt != MOE_W_Q8_0 && m.fmt != MOE_W_Q2SM)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown weight format %d", name, m.fmt);
+  if ((m.fmt == MOE_W_Q2SM && !allow_q2sm) || (m.fmt == MOE_W_F32 && !allow_f32))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: format %s is not supported here", name,
+                m.fmt == MOE_W_F32 ? "F32" : "Q2SM");
+  if (m.rows != rows || m.cols != cols)
+    return fail(MOE_ERR_ARG, "%s: shape %dx%d, expected %dx%d", name, m.rows, m.cols, rows, cols);
+  if (!m.codes) return fail(MOE_ERR_ARG, "%s: codes is NULL", name);
+  if (m.fmt != MOE_W_F32 && !m.scales) return fail(MOE_ERR_ARG, "%s: scales is NULL", name);
+  if (!aligned16(m.codes) || (m.scales && !aligned16(m.scales)))
+    return fail(MOE_ERR_ARG, "%s: code and scale planes must be 16-byte aligned", name);
+  return MOE_OK;
+}
+
+}  // namespace
+
+namespace moe {
+void trace_pre(const char* name, hipStream_t s) {
+  Trace& t = g_trace;
+  if (t.n > 0 && *t.count < t.n && t.name == name) (void)hipEventRecord(t.start[*t.count], s);
+}
+void trace_post(const char* name, hipStream_t s) {
+  Trace& t = g_trace;
+  if (t.n > 0 && *t.count < t.n && t.name == name) {
+    (void)hipEventRecord(t.stop[*t.count], s);
+    ++*t.count;
+  }
+}
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_trace_kernel(const char* name, hipEvent_t* start, hipEvent_t* stop, int32_t n, int32_t* count) {
+  if (n <= 0) {
+    g_trace = Trace{};
+    return ok();
+  }
+  if (!name || !start || !stop || !count) return fail(MOE_ERR_ARG, "moe_trace_kernel: NULL argument");
+  g_trace.name = name;
+  g_trace.start = start;
+  g_trace.stop = stop;
+  g_trace.n = n;
+  g_trace.count = count;
+  *count = 0;
+  return ok();
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+const char* moe_version(void) { return "moe-gfx950 0.1"; }
+
+moe_status moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t k, int32_t E, int32_t E_local, int32_t xt,
+                              size_t* route_ws, size_t* group_ws, size_t* forward_ws) {
+  (void)H;
+  (void)E_local;
+  if (T < 0 || I <= 0 || k <= 0 || E <= 0) return fail(MOE_ERR_ARG, "moe_workspace_size: bad sizes");
+  if (route_ws) *route_ws = route_ws_bytes(T, E);
+  if (group_ws) *group_ws = 0;
+  if (forward_ws) *forward_ws = fwd_layout(T, I, k, E, xt).total;
+  return ok();
+}
+
+moe_status moe_route(const void* x, int32_t xt, int32_t T, int32_t H, const moe_qmat* router, const float* bias,
+                     int32_t k, int32_t* ids, float* w, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (T < 0) return fail(MOE_ERR_ARG, "moe_route: T < 0");
+  if (xt != MOE_ACT_F32 && xt != MOE_ACT_BF16) return fail(MOE_ERR_ARG, "moe_route: unknown activation type %d", xt);
+  if (!router) return fail(MOE_ERR_ARG, "moe_route: router is NULL");
+  if (H <= 0 || H % 32) return fail(MOE_ERR_ARG, "moe_route: H = %d is not a positive multiple of 32", H);
+  if (H > kMaxRouteH) return fail(MOE_ERR_UNSUPPORTED, "moe_route: H = %d exceeds %d", H, kMaxRouteH);
+  const int E = router->rows;
+  if (E < 1) return fail(MOE_ERR_ARG, "moe_route: router has %d rows", E);
+  if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "moe_route: E = %d exceeds %d", E, kMaxE);
+  moe_status st = check_qmat(*router, "router", E, H, false, true);
+  if (st) return st;
+  if (k < 1 || k > E) return fail(MOE_ERR_ARG, "moe_route: k = %d outside 1..E (E = %d)", k, E);
+  if (k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "moe_route: k = %d exceeds %d", k, kMaxK);
+  if (T > 0 && (!x || !ids || !w)) return fail(MOE_ERR_ARG, "moe_route: x, ids and w must not be NULL");
+  if (!aligned16(x)) return fail(MOE_ERR_ARG, "moe_route: x must be 16-byte aligned");
+  const size_t need = route_ws_bytes(T, E);
+  if (ws_bytes < need || (need && !ws))
+    return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu bytes, need %zu", ws_bytes, need);
+  if (T == 0) return ok();
+  DevCheck dc;
+  if ((st = stream_device(s, &dc.dev))) return st;
+  dc(x, "x");
+  dc(router->codes, "router codes");
+  dc(router->scales, "router scales");
+  dc(bias, "bias");
+  dc(ids, "ids");
+  dc(w, "w");
+  dc(ws, "workspace");
+  if (dc.st) return dc.st;
+  hipError_t e = moe::launch_route(x, xt, T, H, router->fmt, qm(*router), bias, k, ids, w,
+                                   reinterpret_cast<float*>(ws), s);
+  if (e != hipSuccess) return hip_fail(e, "moe_route launch");
+  return ok();
+}
+
+moe_status moe_group_tokens(const int32_t* ids, int32_t T, int32_t k, int32_t E, int32_t* counts, int32_t* offsets,
+                            int32_t* slot_list, void* ws, size_t ws_bytes, hipStream_t s) {
+  (void)ws;
+  (void)ws_bytes;
+  if (T < 0 || k < 1) return fail(MOE_ERR_ARG, "moe_group_tokens: T = %d, k = %d", T, k);
+  if (E < 1) return fail(MOE_ERR_ARG, "moe_group_tokens: E = %d", E);
+  if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "moe_group_tokens: E = %d exceeds %d", E, kMaxE);
+  if ((int64_t)T * k > (int64_t)0x7FFFFFFF) return fail(MOE_ERR_ARG, "moe_group_tokens: T*k overflows int32");
+  if (!counts || !offsets || (T > 0 && (!ids || !slot_list)))
+    return fail(MOE_ERR_ARG, "moe_group_tokens: NULL output or ids");
+  moe_status st;
+  DevCheck dc;
+  if ((st = stream_device(s, &dc.dev))) return st;
+  dc(ids, "ids");
+  dc(counts, "counts");
+  dc(offsets, "offsets");
+  dc(slot_list, "slot_list");
+  if (dc.st) return dc.st;
+  const size_t lds = moe::group_lds_bytes(E);
+  if (lds > 64 * 1024) {
+    // more than the default dynamic LDS for large expert counts (set per call: cheap, per device)
+    hipError_t e = moe::group_set_lds_limit(lds);
+    if (e != hipSuccess) return hip_fail(e, "moe_group_tokens: LDS attribute");
+  }
+  hipError_t e = moe::launch_group(ids, T, k, E, counts, offsets, slot_list, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_group_tokens launch");
+  return ok();
+}
+
+moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, int32_t I, int32_t k,
+                              const moe_experts* local, const int32_t* g2l, int32_t E, int32_t E_local,
+                              const int32_t* counts, const int32_t* offsets, const int32_t* slot_list, float* y_slot,
+                              void* ws, size_t ws_bytes, hipStream_t s) {
+  if (T < 0) return fail(MOE_ERR_ARG, "moe_expert_forward: T < 0");
+  if (xt != MOE_ACT_F32 && xt != MOE_ACT_BF16)
+    return fail(MOE_ERR_ARG, "moe_expert_forward: unknown activation type %d", xt);
+  if (H <= 0 || H % 32 || I <= 0 || I % 32)
+    return fail(MOE_ERR_ARG, "moe_expert_forward: H = %d, I = %d must be positive multiples of 32", H, I);
+  if (H > kMaxFfnDim || I > kMaxFfnDim)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_forward: H and I are limited to %d", kMaxFfnDim);
+  if (k < 1 || k > kMaxK) return fail(MOE_ERR_ARG, "moe_expert_forward: k = %d", k);
+  if (E < 1 || k > E) return fail(MOE_ERR_ARG, "moe_expert_forward: E = %d, k = %d", E, k);
+  if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "moe_expert_forward: E = %d exceeds %d", E, kMaxE);
+  if (!local) return fail(MOE_ERR_ARG, "moe_expert_forward: local experts is NULL");
+  if (local->n_experts != E_local || E_local < 1 || E_local > E)
+    return fail(MOE_ERR_ARG, "moe_expert_forward: E_local = %d but the owned stack holds %d experts (E = %d)",
+                E_local, local->n_experts, E);
+  if (!g2l && E_local != E)
+    return fail(MOE_ERR_ARG, "moe_expert_forward: no g2l table but only %d of %d experts owned", E_local, E);
+  moe_status st;
+  if ((st = check_qmat(local->gate, "gate", I, H, true, false))) return st;
+  if ((st = check_qmat(local->up, "up", I, H, true, false))) return st;
+  if ((st = check_qmat(local->down, "down", H, I, true, false))) return st;
+  if (local->gate.fmt != local->up.fmt)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_forward: gate and up must share a format");
+  if (T > 0 && (!x || !counts || !offsets || !slot_list || !y_slot))
+    return fail(MOE_ERR_ARG, "moe_expert_forward: NULL x, counts, offsets, slot_list or y_slot");
+  if (!aligned16(x) || !aligned16(y_slot))
+    return fail(MOE_ERR_ARG, "moe_expert_forward: x and y_slot must be 16-byte aligned");
+  if (xt == MOE_ACT_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_forward: bf16 activations are not built yet");
+  const FwdLayout L = fwd_layout(T, I, k, E, xt);
+  if (ws_bytes < L.total || !ws)
+    return fail(MOE_ERR_WORKSPACE, "moe_expert_forward: workspace %zu bytes, need %zu", ws_bytes, L.total);
+  if (T == 0) return ok();
+  DevCheck dc;
+  if ((st = stream_device(s, &dc.dev))) return st;
+  dc(x, "x");
+  dc(local->gate.codes, "gate codes");
+  dc(local->gate.scales, "gate scales");
+  dc(local->up.codes, "up codes");
+  dc(local->up.scales, "up scales");
+  dc(local->down.codes, "down codes");
+  dc(local->down.scales, "down scales");
+  dc(g2l, "g2l");
+  dc(counts, "counts");
+  dc(offsets, "offsets");
+  dc(slot_list, "slot_list");
+  dc(y_slot, "y_slot");
+  dc(ws, "workspace");
+  if (dc.st) return dc.st;
+
+  char* wsb = reinterpret_cast<char*>(ws);
+  int32_t* n_act = reinterpret_cast<int32_t*>(wsb + L.n_act);
+  int32_t* act = reinterpret_cast<int32_t*>(wsb + L.act);
+  float* h = reinterpret_cast<float*>(wsb + L.h);
+  const int max_active = (int)std::min<int64_t>(E_local, (int64_t)T * k);
+  hipError_t e = moe::launch_active(counts, g2l, E, E_local, act, n_act, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: active-expert launch");
+  e = moe::launch_gemv_forward(reinterpret_cast<const float*>(x), T, H, I, k, qm(local->gate), qm(local->up),
+                               local->gate.fmt, qm(local->down), local->down.fmt, g2l, offsets, slot_list, act,
+                               n_act, max_active, h, y_slot, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: GEMV launch");
+  return ok();
+}
+
+moe_status moe_combine(const float* y_slot, const float* w, const int32_t* ids, const int32_t* g2l, int32_t T,
+                       int32_t k, int32_t H, int32_t E, float* out, hipStream_t s) {
+  if (T < 0 || k < 1 || E < 1) return fail(MOE_ERR_ARG, "moe_combine: T = %d, k = %d, E = %d", T, k, E);
+  if (H <= 0 || H % 4) return fail(MOE_ERR_ARG, "moe_combine: H = %d must be a positive multiple of 4", H);
+  if (T > 0 && (!y_slot || !w || !ids || !out)) return fail(MOE_ERR_ARG, "moe_combine: NULL pointer");
+  if (!aligned16(y_slot) || !aligned16(out)) return fail(MOE_ERR_ARG, "moe_combine: y_slot and out must be 16-byte aligned");
+  if (T == 0) return ok();
+  moe_status st;
+  DevCheck dc;
+  if ((st = stream_device(s, &dc.dev))) return st;
+  dc(y_slot, "y_slot");
+  dc(w, "w");
+  dc(ids, "ids");
+  dc(g2l, "g2l");
+  dc(out, "out");
+  if (dc.st) return dc.st;
+  hipError_t e = moe::launch_combine(y_slot, w, ids, g2l, T, k, H, E, out, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_combine launch");
+  return ok();
+}
+
+// ---- host helpers ---------------------------------------------------------------
+
+moe_status moe_planar_bytes(int32_t fmt, int32_t rows, int32_t cols, size_t* codes_bytes, size_t* scales_bytes) {
+  if (rows < 0 || cols <= 0 || cols % 32) return fail(MOE_ERR_ARG, "moe_planar_bytes: bad shape %dx%d", rows, cols);
+  size_t c, sc;
+  const size_t nb = (size_t)rows * (cols / 32);
+  switch (fmt) {
+    case MOE_W_F32: c = (size_t)rows * cols * 4; sc = 0; break;
+    case MOE_W_Q8_0: c = (size_t)rows * cols; sc = nb * 2; break;
+    case MOE_W_Q2SM: c = (size_t)rows * cols / 4; sc = nb * 4; break;
+    default: return fail(MOE_ERR_UNSUPPORTED, "moe_planar_bytes: unknown format %d", fmt);
+  }
+  if (codes_bytes) *codes_bytes = c;
+  if (scales_bytes) *scales_bytes = sc;
+  return ok();
+}
+
+moe_status moe_pack_planar(int32_t fmt, int32_t n, int32_t rows, int32_t cols, const void* aos, void* codes,
+                           void* scales) {
+  if (n < 0 || rows < 0 || cols <= 0 || cols % 32) return fail(MOE_ERR_ARG, "moe_pack_planar: bad shape");
+  if (!aos || !codes || (fmt != MOE_W_F32 && !scales)) return fail(MOE_ERR_ARG, "moe_pack_planar: NULL pointer");
+  const int64_t nb = cols / 32;
+  const int64_t blocks = (int64_t)n * rows * nb;
+  const uint8_t* src = static_cast<const uint8_t*>(aos);
+  uint8_t* dc = static_cast<uint8_t*>(codes);
+  uint8_t* ds = static_cast<uint8_t*>(scales);
+  switch (fmt) {
+    case MOE_W_F32:
+      std::memcpy(dc, src, (size_t)blocks * 128);
+      break;
+    case MOE_W_Q8_0:
+      for (int64_t b = 0; b < blocks; ++b) {
+        std::memcpy(ds + 2 * b, src + 34 * b, 2);
+        std::memcpy(dc + 32 * b, src + 34 * b + 2, 32);
+      }
+      break;
+    case MOE_W_Q2SM:
+      for (int64_t b = 0; b < blocks; ++b) {
+        std::memcpy(ds + 4 * b, src + 12 * b, 4);
+        std::memcpy(dc + 8 * b, src + 12 * b + 4, 8);
+      }
+      break;
+    default:
+      return fail(MOE_ERR_UNSUPPORTED, "moe_pack_planar: unknown format %d", fmt);
+  }
+  return ok();
+}
+
+moe_status moe_place_lpt(const int64_t* load, int32_t E, int32_t n_shares, int32_t* owner) {
+  if (!load || !owner) return fail(MOE_ERR_ARG, "moe_place_lpt: NULL pointer");
+  if (E < 1 || n_shares < 1 || E % n_shares)
+    return fail(MOE_ERR_ARG, "moe_place_lpt: E = %d is not a positive multiple of n_shares = %d", E, n_shares);
+  std::vector<int> order(E);
+  for (int e = 0; e < E; ++e) order[e] = e;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return load[a] > load[b]; });
+  const int cap = E / n_shares;
+  std::vector<int64_t> sl(n_shares, 0);
+  std::vector<int> sn(n_shares, 0);
+  for (int e : order) {
+    int best = -1;
+    for (int sh = 0; sh < n_shares; ++sh) {
+      if (sn[sh] >= cap) continue;
+      if (best < 0 || sl[sh] < sl[best]) best = sh;
+    }
+    owner[e] = best;
+    sl[best] += load[e];
+    sn[best] += 1;
+  }
+  return ok();
+}
+
+moe_status moe_share_tables(const int32_t* owner, int32_t E, int32_t share, const int32_t* local_order, int32_t* g2l,
+                            int32_t* l2g, int32_t* E_local) {
+  if (!owner || !g2l || !l2g || !E_local || E < 1) return fail(MOE_ERR_ARG, "moe_share_tables: bad arguments");
+  std::vector<int> owned;
+  for (int e = 0; e < E; ++e)
+    if (owner[e] == share) owned.push_back(e);
+  if (local_order)
+    std::stable_sort(owned.begin(), owned.end(), [&](int a, int b) { return local_order[a] < local_order[b]; });
+  for (int e = 0; e < E; ++e) g2l[e] = -1;
+  for (size_t l = 0; l < owned.size(); ++l) {
+    g2l[owned[l]] = (int32_t)l;
+    l2g[l] = owned[l];
+  }
+  *E_local = (int32_t)owned.size();
+  return ok();
+}
+
+moe_status moe_plan_check(const int32_t* g2l, int32_t E, int32_t E_local) {
+  if (!g2l || E < 1 || E_local < 0 || E_local > E) return fail(MOE_ERR_ARG, "moe_plan_check: bad arguments");
+  std::vector<char> seen(E_local, 0);
+  int owned = 0;
+  for (int e = 0; e < E; ++e) {
+    const int l = g2l[e];
+    if (l == -1) continue;
+    if (l < 0 || l >= E_local) return fail(MOE_ERR_ARG, "moe_plan_check: g2l[%d] = %d outside -1..%d", e, l, E_local - 1);
+    if (seen[l]) return fail(MOE_ERR_ARG, "moe_plan_check: local id %d owned twice", l);
+    seen[l] = 1;
+    ++owned;
+  }
+  if (owned != E_local)
+    return fail(MOE_ERR_ARG, "moe_plan_check: %d experts owned but E_local = %d", owned, E_local);
+  return ok();
+}
+
+}  // extern "C"

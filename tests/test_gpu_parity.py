@@ -1,0 +1,163 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Expert ids and groupings must match bit for bit; floating-point outputs
+within max|d| <= 2e-3 max|ref| and rel-L2 <= 1e-4 (tests/helpers.py)."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import assert_close, oracle_expect, sha
+from gpu_util import make_layer, run, torch_mod, x_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def check_against_oracle(wl, got, ref, slots_checked=None, what=""):
+    T, k = wl.T, wl.k
+    tok = ref["tokens"]
+    assert np.array_equal(got["ids"][tok], ref["ids"]), f"{what}: expert ids differ"
+    assert_close(got["w"][tok], ref["w"], f"{what} weights")
+    if len(tok) == T:
+        counts, offsets, slots = oracle.group(ref["ids"], wl.E)
+        assert np.array_equal(got["counts"], counts), f"{what}: counts differ"
+        assert np.array_equal(got["offsets"], offsets), f"{what}: offsets differ"
+        assert np.array_equal(got["slot_list"], slots), f"{what}: slot_list differs"
+    # y rows of the checked tokens' (owned) slots
+    rows = np.concatenate([np.arange(t * k, (t + 1) * k) for t in tok])
+    ref_y = ref["y"]
+    owned = ~np.isnan(ref_y[:, 0])
+    if owned.any():
+        assert_close(got["y"][rows][owned], ref_y[owned], f"{what} y_slot")
+    assert_close(got["out"][tok], ref["out"], f"{what} out")
+
+
+@pytest.fixture(scope="module")
+def torch():
+    return torch_mod()
+
+
+def test_cfg1_tiny(torch):
+    _say("cfg1 tiny T=4")
+    wl = synth.make(1)
+    got = run(make_layer(wl), wl, torch)
+    check_against_oracle(wl, got, oracle_expect(wl), what="cfg1")
+
+
+@pytest.mark.parametrize("T", [1, 5])
+def test_cfg2_decode(torch, T):
+    _say(f"cfg2 decode T={T}")
+    wl = synth.make(2, T=T)
+    got = run(make_layer(wl), wl, torch)
+    check_against_oracle(wl, got, oracle_expect(wl), what=f"cfg2 T={T}")
+
+
+def test_cfg3_batched_decode(torch):
+    _say("cfg3 batched decode T=32")
+    wl = synth.make(3)
+    got = run(make_layer(wl), wl, torch)
+    check_against_oracle(wl, got, oracle_expect(wl), what="cfg3")
+    assert np.count_nonzero(got["counts"]) > 32      # the bias spreads load over many experts
+
+
+def test_cfg3_ragged_tokens(torch):
+    _say("cfg3 shapes, ragged T=37")
+    wl = synth.make(3, T=37)
+    got = run(make_layer(wl), wl, torch)
+    check_against_oracle(wl, got, oracle_expect(wl, tokens=list(range(0, 37, 3))), what="cfg3 T=37")
+
+
+def test_cfg5_shares_sum_to_full(torch):
+    _say("cfg5 shares T=128")
+    import quantized_moe_routed_amd as moe
+    wl = synth.make(5)
+    owner = moe.place_lpt(wl.load_hist, 2)
+    assert np.array_equal(owner, oracle.place_lpt(wl.load_hist, 2))
+    sample = list(range(0, 128, 4))
+    full_ref = oracle_expect(wl, tokens=sample)
+    parts = []
+    for share in (0, 1):
+        g2l, l2g = moe.share_tables(owner, share)
+        assert len(l2g) == 128
+        _say(f"cfg5 share {share}")
+        got = run(make_layer(wl, l2g=l2g, g2l=g2l), wl, torch)
+        ref = oracle_expect(wl, tokens=sample, l2g=l2g, g2l=g2l)
+        check_against_oracle(wl, got, ref, what=f"cfg5 share {share}")
+        # the permuted placement (local 0 != global 0) gives a bit-identical partial
+        g2l_p, l2g_p = moe.share_tables(owner, share, wl.local_perm)
+        assert np.any(l2g_p != l2g)
+        got_p = run(make_layer(wl, l2g=l2g_p, g2l=g2l_p), wl, torch)
+        assert got_p["out"].tobytes() == got["out"].tobytes()
+        parts.append(got["out"])
+    total = parts[0].astype(np.float64) + parts[1].astype(np.float64)
+    assert_close(total[sample], full_ref["out"], "cfg5 partial A + partial B vs full")
+    # and the sum against the GPU's own full layer, on every token
+    full_gpu = run(make_layer(wl), wl, torch)
+    assert_close(total, full_gpu["out"], "cfg5 A + B vs GPU full")
+
+
+def test_repeat_runs_are_bit_identical(torch):
+    _say("determinism cfg3 x5")
+    wl = synth.make(3)
+    layer = make_layer(wl)
+    x = x_tensor(wl, torch)
+    hashes = set()
+    for _ in range(5):
+        g = run(layer, wl, torch, x)
+        hashes.add(sha(g["ids"], g["w"], g["counts"], g["offsets"], g["slot_list"], g["y"], g["out"]))
+    assert len(hashes) == 1
+
+
+def test_small_shapes_and_edge_cases(torch):
+    _say("edge cases")
+    # 5 router blocks (padded tree), fp32 router, Q8_0 experts, k = 1
+    cfg = synth.custom(9, 160, 8, 96, 1, router_fmt=0)
+    wl = synth.make(cfg)
+    got = run(make_layer(wl), wl, torch)
+    check_against_oracle(wl, got, oracle_expect(wl), what="H=160 k=1")
+    assert np.all(got["w"] == 1.0)
+    # Q2SM experts with Q8_0 router and bias, odd number of blocks in a row (H = 2080)
+    cfg = synth.custom(6, 2080, 16, 224, 3, gate_fmt=2, up_fmt=2, down_fmt=2, router_fmt=1, bias="normal0.5")
+    wl = synth.make(cfg)
+    got = run(make_layer(wl), wl, torch)
+    check_against_oracle(wl, got, oracle_expect(wl), what="H=2080 odd blocks")
+
+
+def test_zero_router_ties_go_to_lower_ids(torch):
+    _say("ties")
+    wl = synth.make(1)
+    wl.router = np.zeros_like(wl.router)          # fp32 zero router: every logit is 0
+    got = run(make_layer(wl), wl, torch)
+    assert np.array_equal(got["ids"], np.tile(np.arange(2), (wl.T, 1)))
+    assert np.all(got["w"] == 0.5)
+
+
+def test_t0_is_a_no_op(torch):
+    _say("T=0")
+    wl = synth.make(1, T=0)
+    layer = make_layer(wl)
+    x = torch.empty((0, wl.H), dtype=torch.float32, device="cuda")
+    b = layer.buffers(0, 0)
+    layer.run(x, b)
+    torch.cuda.synchronize()
+    assert b.counts.cpu().numpy().sum() == 0
+
+
+def test_host_pointer_is_rejected(torch):
+    _say("device check")
+    import quantized_moe_routed_amd as moe
+    wl = synth.make(1)
+    layer = make_layer(wl)
+    b = layer.buffers(wl.T, 0)
+    host_x = np.ascontiguousarray(wl.x)
+    with pytest.raises(moe.MoeError) as e:
+        moe.route(host_x, 0, wl.T, wl.H, layer._router_q, None, wl.k, b.ids, b.w, b.route_ws,
+                  b.route_ws.numel())
+    assert e.value.status == moe.ERR_DEVICE
