@@ -149,8 +149,12 @@ moe_status moe_group_tokens(const int32_t* ids, int32_t T, int32_t k, int32_t E,
  *             slots, rows of unowned slots are left untouched.
  * E_local must equal local->n_experts; the table's consistency is checked once
  * on the host with moe_plan_check().  fp32 activations run the dequant-GEMV
- * kernels; bf16 activations run the grouped MFMA GEMM, whose intermediate
- * silu(g)*u keeps fp32 precision (a bf16 hi/lo pair).
+ * kernels (gate/up Q8_0 or Q2SM, down Q8_0 or Q2SM).  bf16 activations run the
+ * grouped bf16 MFMA GEMM: it needs Q2SM gate/up, a Q8_0 down projection and H, I
+ * multiples of 64 (else MOE_ERR_UNSUPPORTED); weight codes enter the matrix
+ * cores exactly, block scales are applied in fp32 per 32-block, and the
+ * intermediate silu(g)*u enters the down projection as a bf16 hi/lo pair
+ * (16 significant bits).  No path uses floating-point atomics.
  * Limits: H and I multiples of 32, H <= 8192, I <= 8192. */
 moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, int32_t I, int32_t k,
                               const moe_experts* local, const int32_t* g2l, int32_t E, int32_t E_local,
@@ -170,7 +174,8 @@ moe_status moe_combine(const float* y_slot, const float* w, const int32_t* ids, 
  * `name` gets hipEventRecord(start[i]) before and hipEventRecord(stop[i])
  * after it on the call's stream, for i < n; *count holds how many launches
  * were recorded.  Kernel names: route_logits, route_topk, group, active,
- * gemv_gateup, gemv_down, combine.  The caller owns the events and must keep
+ * gemv_gateup, gemv_down, block_sums, gemm_tiles, gemm_gateup, gemm_down,
+ * combine.  The caller owns the events and must keep
  * them, and count, alive while tracing; n <= 0 switches tracing off. */
 moe_status moe_trace_kernel(const char* name, hipEvent_t* start, hipEvent_t* stop, int32_t n, int32_t* count);
 

@@ -22,6 +22,7 @@ SOURCES = {
     "route.hip": ["-ffp-contract=off"],
     "group.hip": [],
     "gemv.hip": [],
+    "gemm.hip": [],
     "combine.hip": [],
     "api.cpp": [],
 }

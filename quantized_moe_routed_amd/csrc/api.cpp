@@ -97,18 +97,27 @@ moe::QMat qm(const moe_qmat& m) { return moe::QMat{m.codes, m.scales, m.rows, m.
 // ---- workspace layouts -------------------------------------------------------
 size_t route_ws_bytes(int T, int E) { return align_up((size_t)T * E * sizeof(float)); }
 
+// fp32 activations: active-expert list + fp32 h.  bf16 activations: tile
+// list, block sums of x, and h as two bf16 planes (hi, then lo).
 struct FwdLayout {
-  size_t n_act, act, h, total;
+  size_t n_act, act, n_tiles, tiles, xs, h, total;
 };
 
-FwdLayout fwd_layout(int T, int I, int k, int E, int xt) {
-  (void)xt;
-  FwdLayout L;
+FwdLayout fwd_layout(int T, int H, int I, int k, int E, int E_local, int xt) {
+  FwdLayout L{};
   size_t off = 0;
   L.n_act = off;
   off += kAlign;
   L.act = off;
   off += align_up((size_t)E * sizeof(int32_t));
+  if (xt == MOE_ACT_BF16) {
+    L.n_tiles = off;
+    off += kAlign;
+    L.tiles = off;
+    off += align_up((size_t)moe::gemm_max_tiles(T, k, E_local) * 4 * sizeof(int32_t));
+    L.xs = off;
+    off += align_up((size_t)T * (H / 32) * sizeof(float));
+  }
   L.h = off;
   off += align_up((size_t)T * k * I * sizeof(float));
   L.total = off;
@@ -169,12 +178,12 @@ const char* moe_version(void) { return "moe-gfx950 0.1"; }
 
 moe_status moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t k, int32_t E, int32_t E_local, int32_t xt,
                               size_t* route_ws, size_t* group_ws, size_t* forward_ws) {
-  (void)H;
-  (void)E_local;
-  if (T < 0 || I <= 0 || k <= 0 || E <= 0) return fail(MOE_ERR_ARG, "moe_workspace_size: bad sizes");
+  if (T < 0 || H <= 0 || I <= 0 || k <= 0 || E <= 0 || E_local < 0 || E_local > E)
+    return fail(MOE_ERR_ARG, "moe_workspace_size: bad sizes");
+  if (xt != MOE_ACT_F32 && xt != MOE_ACT_BF16) return fail(MOE_ERR_ARG, "moe_workspace_size: unknown activation type");
   if (route_ws) *route_ws = route_ws_bytes(T, E);
   if (group_ws) *group_ws = 0;
-  if (forward_ws) *forward_ws = fwd_layout(T, I, k, E, xt).total;
+  if (forward_ws) *forward_ws = fwd_layout(T, H, I, k, E, E_local, xt).total;
   return ok();
 }
 
@@ -273,9 +282,15 @@ moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, i
     return fail(MOE_ERR_ARG, "moe_expert_forward: NULL x, counts, offsets, slot_list or y_slot");
   if (!aligned16(x) || !aligned16(y_slot))
     return fail(MOE_ERR_ARG, "moe_expert_forward: x and y_slot must be 16-byte aligned");
-  if (xt == MOE_ACT_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_forward: bf16 activations are not built yet");
-  const FwdLayout L = fwd_layout(T, I, k, E, xt);
+  if (xt == MOE_ACT_BF16) {
+    if (H % 64 || I % 64)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_expert_forward: bf16 activations need H and I multiples of 64 (H = %d, I = %d)",
+                  H, I);
+    if (local->gate.fmt != MOE_W_Q2SM || local->down.fmt != MOE_W_Q8_0)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "moe_expert_forward: bf16 activations run Q2SM gate/up with a Q8_0 down projection");
+  }
+  const FwdLayout L = fwd_layout(T, H, I, k, E, E_local, xt);
   if (ws_bytes < L.total || !ws)
     return fail(MOE_ERR_WORKSPACE, "moe_expert_forward: workspace %zu bytes, need %zu", ws_bytes, L.total);
   if (T == 0) return ok();
@@ -297,6 +312,16 @@ moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, i
   if (dc.st) return dc.st;
 
   char* wsb = reinterpret_cast<char*>(ws);
+  if (xt == MOE_ACT_BF16) {
+    uint16_t* h_hi = reinterpret_cast<uint16_t*>(wsb + L.h);
+    uint16_t* h_lo = h_hi + (size_t)T * k * I;
+    hipError_t e = moe::launch_gemm_forward(
+        reinterpret_cast<const uint16_t*>(x), T, H, I, k, qm(local->gate), qm(local->up), qm(local->down), g2l, E,
+        E_local, counts, offsets, slot_list, reinterpret_cast<float*>(wsb + L.xs), reinterpret_cast<int4*>(wsb + L.tiles),
+        reinterpret_cast<int32_t*>(wsb + L.n_tiles), h_hi, h_lo, y_slot, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: GEMM launch");
+    return ok();
+  }
   int32_t* n_act = reinterpret_cast<int32_t*>(wsb + L.n_act);
   int32_t* act = reinterpret_cast<int32_t*>(wsb + L.act);
   float* h = reinterpret_cast<float*>(wsb + L.h);

@@ -29,6 +29,13 @@ hipError_t launch_gemv_forward(const float* x, int T, int H, int I, int k, const
                                const int32_t* offsets, const int32_t* slot_list, const int32_t* act,
                                const int32_t* n_act, int max_active, float* h_ws, float* y, hipStream_t s);
 
+// Grouped MFMA GEMM (bf16 activations).  H and I must be multiples of 64.
+int gemm_max_tiles(int T, int k, int E_local);
+hipError_t launch_gemm_forward(const uint16_t* x, int T, int H, int I, int k, const QMat& gate, const QMat& up,
+                               const QMat& down, const int32_t* g2l, int E, int E_local, const int32_t* counts,
+                               const int32_t* offsets, const int32_t* slot_list, float* xs, int4* tiles,
+                               int32_t* n_tiles, uint16_t* h_hi, uint16_t* h_lo, float* y, hipStream_t s);
+
 hipError_t launch_combine(const float* y, const float* w, const int32_t* ids, const int32_t* g2l, int T, int k,
                           int H, int E, float* out, hipStream_t s);
 

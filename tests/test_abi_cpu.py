@@ -160,3 +160,17 @@ def test_group_and_combine_argument_errors():
     assert _status(lambda: moe.combine(FAKE, FAKE, FAKE, None, 4, 2, 6, 8, FAKE, stream=0)) == moe.ERR_ARG
     assert _status(lambda: moe.combine(None, FAKE, FAKE, None, 4, 2, 256, 8, FAKE, stream=0)) == moe.ERR_ARG
     moe.combine(FAKE, FAKE, FAKE, None, 0, 2, 256, 8, FAKE, stream=0)
+
+
+def test_bf16_forward_shape_and_format_limits():
+    big = 1 << 30
+    def call(H=256, I=128, gf=moe.W_Q2SM, df=moe.W_Q8_0):
+        ex = moe.Experts(moe.qmat(gf, I, H, FAKE, FAKE), moe.qmat(gf, I, H, FAKE, FAKE),
+                         moe.qmat(df, H, I, FAKE, FAKE), 8)
+        moe.expert_forward(FAKE, moe.ACT_BF16, 4, H, I, 2, ex, None, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, big, 0)
+    assert _status(lambda: call(H=160)) == moe.ERR_UNSUPPORTED          # H not a multiple of 64
+    assert _status(lambda: call(I=96)) == moe.ERR_UNSUPPORTED           # I not a multiple of 64
+    assert _status(lambda: call(gf=moe.W_Q8_0)) == moe.ERR_UNSUPPORTED  # MFMA path: Q2SM gate/up
+    assert _status(lambda: call(df=moe.W_Q2SM)) == moe.ERR_UNSUPPORTED  # MFMA path: Q8_0 down
+    a = moe.workspace_size(2048, 4096, 2048, 8, 256, 256, moe.ACT_BF16)
+    assert a[2] >= 2048 * 8 * 2048 * 4 + 2048 * 128 * 4

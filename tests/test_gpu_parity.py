@@ -161,3 +161,68 @@ def test_host_pointer_is_rejected(torch):
         moe.route(host_x, 0, wl.T, wl.H, layer._router_q, None, wl.k, b.ids, b.w, b.route_ws,
                   b.route_ws.numel())
     assert e.value.status == moe.ERR_DEVICE
+
+
+# ---- bf16 activations: the grouped MFMA GEMM ---------------------------------------------
+
+def test_cfg4_prefill_shapes_small_batch(torch):
+    _say("cfg4 prefill shapes, T=96 (tiles of 64 plus a ragged tail)")
+    wl = synth.make(4, T=96)
+    got = run(make_layer(wl), wl, torch)
+    check_against_oracle(wl, got, oracle_expect(wl, tokens=list(range(0, 96, 5))), what="cfg4 T=96")
+
+
+def _sample_tokens(ids, counts, n_each=6):
+    """Tokens routed to the most loaded experts and to the least loaded (non-empty) ones."""
+    order = np.argsort(-counts, kind="stable")
+    heavy = [e for e in order if counts[e] > 0][:2]
+    light = [e for e in order[::-1] if counts[e] > 0][:4]
+    pick = []
+    for e in heavy + light:
+        toks = np.nonzero((ids == e).any(1))[0]
+        pick += [int(t) for t in toks[:n_each]]
+    pick += list(range(0, ids.shape[0], max(1, ids.shape[0] // 8)))
+    return sorted(set(pick))
+
+
+def test_cfg4_prefill_full_size(torch):
+    _say("cfg4 prefill T=2048: ids/grouping for every token, sampled outputs, 5 runs bit-identical")
+    wl = synth.make(4)
+    layer = make_layer(wl)
+    x = x_tensor(wl, torch)
+    got = run(layer, wl, torch, x)
+    ids, w, _ = oracle.route(wl.x, wl.cfg.router_fmt, wl.router[0], wl.bias, wl.k)
+    assert np.array_equal(got["ids"], ids), "expert ids differ"
+    assert_close(got["w"], w, "weights")
+    counts, offsets, slots = oracle.group(ids, wl.E)
+    assert np.array_equal(got["counts"], counts)
+    assert np.array_equal(got["offsets"], offsets)
+    assert np.array_equal(got["slot_list"], slots)
+    assert counts.max() > 2 * 64          # skewed load: the heaviest expert spans several tiles
+    sample = _sample_tokens(ids, counts)
+    _say(f"cfg4 oracle on {len(sample)} sampled tokens; max load {counts.max()}, distinct {np.count_nonzero(counts)}")
+    ref = oracle_expect(wl, tokens=sample)
+    check_against_oracle(wl, got, ref, what="cfg4 T=2048")
+    h0 = sha(got["ids"], got["w"], got["counts"], got["offsets"], got["slot_list"], got["y"], got["out"])
+    for rep in range(4):
+        g = run(layer, wl, torch, x)
+        assert sha(g["ids"], g["w"], g["counts"], g["offsets"], g["slot_list"], g["y"], g["out"]) == h0, rep
+
+
+def test_bf16_small_shapes_and_share(torch):
+    _say("bf16 small shapes: H=128, I=192, E=8, k=3, T=23; then an owned share and its complement")
+    import quantized_moe_routed_amd as moe
+    cfg = synth.custom(23, 128, 8, 192, 3, gate_fmt=2, up_fmt=2, down_fmt=1, router_fmt=1, act="bf16",
+                       bias="normal0.5", name="bf16_small")
+    wl = synth.make(cfg)
+    got = run(make_layer(wl), wl, torch)
+    check_against_oracle(wl, got, oracle_expect(wl), what="bf16 small")
+    owner = np.array([0, 1, 1, 0, 1, 0, 0, 1], np.int32)
+    parts = []
+    for share in (0, 1):
+        g2l, l2g = moe.share_tables(owner, share, np.array([3, 1, 7, 0, 5, 2, 6, 4], np.int32))
+        assert l2g[0] != 0 or share == 1
+        gs = run(make_layer(wl, l2g=l2g, g2l=g2l), wl, torch)
+        check_against_oracle(wl, gs, oracle_expect(wl, l2g=l2g, g2l=g2l), what=f"bf16 share {share}")
+        parts.append(gs["out"].astype(np.float64))
+    assert_close(parts[0] + parts[1], got["out"], "bf16 share A + share B vs full")
