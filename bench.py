@@ -2,14 +2,19 @@
 
 One step = one pass of the whole layer (moe_route, moe_group_tokens,
 moe_expert_forward, moe_combine) over one batch of synthetic input that is
-already resident in device memory.  The default workload is single-token
-decode (T=1, H=4096, 256 experts, I=2048, top-8, 2-bit gate/up/down, Q8_0
-router, fp32 activations): every step routes a different token from a pool of
-distinct tokens, so successive steps touch different experts and the 76.6 MB
-each step reads mostly misses the 256 MB last-level cache, as real decode does.
+already resident in device memory.
 
-Prints one JSON line.  The dominant kernel's time comes from HIP events the
-library records around each of its launches during the timed region.
+The headline workload is single-token decode (T=1, H=4096, 256 experts,
+I=2048, top-8, 2-bit gate/up/down, Q8_0 router, fp32 activations).  Every step
+routes a different token from a pool of distinct tokens, so successive steps
+touch different experts and the 76.6 MB a step reads mostly misses the 256 MB
+last-level cache, as real decode does.  The same JSON line also carries the
+other workloads (batched decode, prefill on bf16 matrix cores, one expert-
+parallel share) measured the same way, under "workloads".
+
+Kernel times come from HIP events that the library records around each launch
+of the named kernel during the timed region (on the stream the kernel runs on).
+Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -25,33 +30,147 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
+
+WORKLOADS = {
+    "decode": 2,
+    "batched_decode": 3,
+    "prefill": 4,
+    "ep_share": 5,
+}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(wl, layer_bytes_per_expert, D, T):
-    """Bytes the layer must move once: the distinct touched experts' weights, the
-    router, the activations in and the output out."""
-    router = wl.router[0].nbytes if wl.cfg.router_fmt != 0 else wl.E * wl.H * 4
-    x_bytes = T * wl.H * (2 if wl.cfg.act == "bf16" else 4)
-    return D * layer_bytes_per_expert + router + x_bytes + T * wl.H * 4
+def build_layer(cfg_id, share=None):
+    """Device layer for a workload (the owned share's stack when share is given)."""
+    import synth
+    import quantized_moe_routed_amd as moe
+    from quantized_moe_routed_amd.layer import MoELayer
+    wl = synth.make(cfg_id, T=1)
+    fm = (wl.cfg.gate_fmt, wl.cfg.up_fmt, wl.cfg.down_fmt)
+    g2l = None
+    gate, up, down = wl.gate, wl.up, wl.down
+    if share is not None:
+        owner = moe.place_lpt(wl.load_hist, 2)
+        g2l, l2g = moe.share_tables(owner, share)
+        gate, up, down = gate[l2g], up[l2g], down[l2g]
+    layer = MoELayer(wl.H, wl.I, wl.E, wl.k, wl.cfg.router_fmt, wl.router[0], wl.bias, fm, gate, up, down,
+                     g2l=g2l)
+    return wl, layer
 
 
-def cpu_baseline(wl_cfg, pool_tokens, budget_s=15.0, max_tokens=400):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+def input_pool(wl, n_batches, torch):
+    """n_batches distinct device batches of the workload's T tokens."""
+    import synth
+    T = wl.cfg.T
+    toks = synth.tokens(0, T * n_batches, wl.H)
+    if wl.cfg.act == "bf16":
+        bits = synth.f32_to_bf16_bits(toks)
+        xs = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        xs = torch.from_numpy(toks).cuda()
+    return [xs[i * T:(i + 1) * T] for i in range(n_batches)], toks
+
+
+def time_layer(layer, xs, steps, warmup, kernel, torch):
+    """Run warmup + steps layer calls cycling through xs; returns the step time
+    (ms), the average duration of `kernel` (ms), and the mean number of owned
+    experts touched and of owned slots per batch."""
+    import quantized_moe_routed_amd as moe
+    from quantized_moe_routed_amd.layer import act_code
+    b = layer.buffers(xs[0].shape[0], act_code(xs[0]))
+    for i in range(warmup):
+        layer.run(xs[i % len(xs)], b)
+    torch.cuda.synchronize()
+    trace = moe.KernelTrace(kernel, steps)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with trace:
+        start.record()
+        for i in range(steps):
+            layer.run(xs[(warmup + i) % len(xs)], b)
+        end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / steps
+    kms = trace.times_ms()
+    # per-step loads, outside the timed region: replay the routing of each batch and
+    # count the owned experts touched and the owned slots
+    owned = None if layer.g2l is None else (layer.g2l >= 0)
+    distinct, slots = [], []
+    for i in range(min(steps, len(xs))):
+        layer.route(xs[(warmup + i) % len(xs)], b)
+        layer.group(b)
+        c = b.counts if owned is None else b.counts * owned
+        distinct.append(int(torch.count_nonzero(c).item()))
+        slots.append(int(c.sum().item()))
+    torch.cuda.synchronize()
+    return ms_step, float(np.mean(kms)), float(np.mean(distinct)), float(np.mean(slots))
+
+
+def measure(name, steps, warmup, torch):
+    cfg_id = WORKLOADS[name]
+    share = 0 if name == "ep_share" else None
+    log(f"{name}: generating weights and inputs")
+    wl, layer = build_layer(cfg_id, share)
+    T, H, I, k = wl.cfg.T, wl.H, wl.I, wl.k
+    n_batches = 1 if name == "prefill" else max(1, 1024 // T)
+    xs, _ = input_pool(wl, n_batches, torch)
+    per_expert = layer.expert_bytes() // layer.E_local
+    gateup_per_expert = (layer.gate.nbytes() + layer.up.nbytes()) // layer.E_local
+    bf16 = wl.cfg.act == "bf16"
+    kernel = "gemm_gateup" if bf16 else "gemv_gateup"
+    log(f"{name}: timing {steps} steps")
+    ms, kms, D_owned, owned_slots = time_layer(layer, xs, steps, warmup, kernel, torch)
+    router_bytes = layer.router.nbytes()
+    x_bytes = T * H * (2 if bf16 else 4)
+    layer_bytes = D_owned * per_expert + router_bytes + x_bytes + T * H * 4
+    flops = 6.0 * H * I * owned_slots
+    res = {
+        "tokens_per_s": T / (ms * 1e-3),
+        "ms_per_step": ms,
+        "T": T,
+        "distinct_experts": D_owned,
+        "owned_slots": owned_slots,
+        "layer_bytes": layer_bytes,
+        "layer_gbs": layer_bytes / (ms * 1e-3) / 1e9,
+        "layer_tflops": flops / (ms * 1e-3) / 1e12,
+        "mfma_frac_of_bf16_peak": (flops / (ms * 1e-3) / 1e12) / BF16_PEAK_TFLOPS if bf16 else None,
+        "kernel": kernel,
+        "kernel_avg_ms": kms,
+    }
+    if bf16:
+        # gate/up: 2 matrices x 2 flops x H x I per owned slot
+        kflops = 4.0 * H * I * owned_slots
+        res["roofline"] = {"bound": "mfma", "achieved": kflops / (kms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": kflops / (kms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                           "traffic": None, "algorithmic_flops_per_launch": kflops}
+    else:
+        # gate/up weights of the touched experts, x once per owned slot, h written once per slot
+        kbytes = D_owned * gateup_per_expert + owned_slots * (H * 4 + I * 4)
+        res["roofline"] = {"bound": "hbm", "achieved": kbytes / (kms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": kbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                           "algorithmic_bytes_per_launch": kbytes}
+    res["roofline"]["kernel"] = kernel
+    res["roofline"]["avg_launch_ms"] = kms
+    return wl, res
+
+
+def cpu_baseline(budget_s=15.0, max_tokens=400):
+    """The CPU oracle, as it stands, on a bounded sample of the decode workload."""
     import oracle
     import synth
-    wl = synth.make(wl_cfg, T=1)
+    wl = synth.make(2, T=1)
     fm = (wl.cfg.gate_fmt, wl.cfg.up_fmt, wl.cfg.down_fmt)
+    pool = synth.tokens(0, max_tokens, wl.H)
     done = 0
     t0 = time.perf_counter()
     while done < max_tokens and time.perf_counter() - t0 < budget_s:
-        n = 8
-        xs = pool_tokens[done:done + n]
+        xs = pool[done:done + 8]
         oracle.layer(xs, wl.cfg.router_fmt, wl.router[0], wl.bias, wl.k, fm, wl.gate, wl.up, wl.down)
         done += len(xs)
     dt = time.perf_counter() - t0
@@ -66,7 +185,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--pool", type=int, default=1024, help="distinct tokens cycled through (decode)")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode",
+                    help="workload of the headline value (default: single-token decode)")
+    ap.add_argument("--only", action="store_true", help="measure the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -75,80 +196,55 @@ def main():
         sys.exit(2)
 
     import torch
-    import synth
-    import quantized_moe_routed_amd as moe
-    from quantized_moe_routed_amd.layer import MoELayer
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
 
-    assert torch.cuda.is_available()
-    cfg_id = 2
-    log("generating decode workload (256 experts, 2-bit)")
-    wl = synth.make(cfg_id, T=1)
-    fm = (wl.cfg.gate_fmt, wl.cfg.up_fmt, wl.cfg.down_fmt)
-    layer = MoELayer(wl.H, wl.I, wl.E, wl.k, wl.cfg.router_fmt, wl.router[0], wl.bias, fm, wl.gate, wl.up,
-                     wl.down)
-    bytes_per_expert = layer.expert_bytes() // wl.E
-    gateup_bytes_per_expert = (layer.gate.nbytes() + layer.up.nbytes()) // wl.E
-    pool = synth.tokens(0, args.pool, wl.H)
-    x_pool = torch.from_numpy(pool).cuda()
-    xs = [x_pool[i:i + 1] for i in range(args.pool)]
-    b = layer.buffers(1, moe.ACT_F32)
-    log("warmup")
-    for i in range(args.warmup):
-        layer.run(xs[i % args.pool], b)
-    torch.cuda.synchronize()
-
-    K = args.steps
-    dom = "gemv_gateup"
-    trace = moe.KernelTrace(dom, K)
-    distinct = []
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    log(f"timing {K} steps")
-    with trace:
-        start.record()
-        for i in range(K):
-            layer.run(xs[(args.warmup + i) % args.pool], b)
-        end.record()
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / K
-    dom_ms = trace.times_ms()
-    dom_avg_ms = float(np.mean(dom_ms))
-    D = int(np.count_nonzero(b.counts.cpu().numpy()))
-    distinct.append(D)
-
-    T = 1
-    layer_bytes = algorithmic_bytes(wl, bytes_per_expert, D, T)
-    # gate/up kernel: gate + up weights of the touched experts, x read once per slot, h written
-    dom_bytes = D * gateup_bytes_per_expert + T * wl.k * wl.H * 4 + T * wl.k * wl.I * 4
-    dom_gbs = dom_bytes / (dom_avg_ms * 1e-3) / 1e9
+    wl, head = measure(args.workload, args.steps, args.warmup, torch)
+    others = {}
+    if not args.only:
+        for name in ("batched_decode", "prefill", "ep_share", "decode"):
+            if name == args.workload:
+                continue
+            steps = {"prefill": 20, "batched_decode": 100, "ep_share": 50, "decode": 200}[name]
+            _, r = measure(name, steps, 5, torch)
+            others[name] = r
+    T = head["T"]
+    cfg = wl.cfg
+    desc = {
+        "decode": "single-token decode: T=1, H=4096, E=256 routed experts, I=2048, top-8, Q2SM (2-bit) "
+                  "gate/up/down, Q8_0 router, fp32 activations, distinct tokens cycled",
+        "batched_decode": "batched decode: T=32, H=4096, E=256, I=2048, top-8, Q2SM gate/up, Q8_0 down, "
+                          "router bias N(0,0.5), fp32 activations",
+        "prefill": "prefill: T=2048, H=4096, E=256, I=2048, top-8, Q2SM gate/up, Q8_0 down, Zipf(1.1) router "
+                   "bias, bf16 activations on matrix cores",
+        "ep_share": "expert-parallel share: T=128, 128 of 256 experts owned (LPT), H=4096, I=2048, top-8, "
+                    "Q2SM gate/up, Q8_0 down, fp32 activations; partial output",
+    }[args.workload]
     result = {
         "metric": "MoE layer tokens/s at 1 MI355X; decode HBM GB/s and prefill MFMA % of peak",
-        "value": T / (ms_step * 1e-3),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if cfg.act == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": "single-token decode: T=1, H=4096, E=256 routed experts, I=2048, top-8, "
-                               "Q2SM (2-bit) gate/up/down, Q8_0 router, fp32 activations, "
-                               f"{args.pool} distinct tokens cycled",
-                   "global_batch": T, "parallelism": "none (1 GPU)"},
-        "layer_gbs": layer_bytes / (ms_step * 1e-3) / 1e9,
-        "layer_bytes_per_step": layer_bytes,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dom_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": dom_avg_ms},
+        "config": {"workload": desc, "global_batch": T, "parallelism": "none (1 GPU)"},
+        "layer_gbs": head["layer_gbs"],
+        "layer_bytes_per_step": head["layer_bytes"],
+        "distinct_experts_per_step": head["distinct_experts"],
+        "roofline": head["roofline"],
     }
-    if not args.no_cpu_baseline:
+    if head["mfma_frac_of_bf16_peak"] is not None:
+        result["mfma_frac_of_bf16_peak"] = head["mfma_frac_of_bf16_peak"]
+    if others:
+        result["workloads"] = others
+    if not args.no_cpu_baseline and args.workload == "decode":
         log("cpu baseline (oracle on a bounded sample)")
-        result["cpu_baseline"] = cpu_baseline(cfg_id, pool)
+        result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
 
 
