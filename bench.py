@@ -123,7 +123,7 @@ def measure(name, steps, warmup, torch):
     per_expert = layer.expert_bytes() // layer.E_local
     gateup_per_expert = (layer.gate.nbytes() + layer.up.nbytes()) // layer.E_local
     bf16 = wl.cfg.act == "bf16"
-    kernel = "gemm_gateup" if bf16 else "gemv_gateup"
+    kernel = "ffn_gateup"
     log(f"{name}: timing {steps} steps")
     ms, kms, D_owned, owned_slots = time_layer(layer, xs, steps, warmup, kernel, torch)
     router_bytes = layer.router.nbytes()

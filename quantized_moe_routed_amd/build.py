@@ -21,8 +21,8 @@ ARCH = "gfx950"
 SOURCES = {
     "route.hip": ["-ffp-contract=off"],
     "group.hip": [],
-    "gemv.hip": [],
-    "gemm.hip": [],
+    "prep.hip": [],
+    "ffn.hip": [],
     "combine.hip": [],
     "api.cpp": [],
 }

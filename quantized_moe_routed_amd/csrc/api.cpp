@@ -97,29 +97,44 @@ moe::QMat qm(const moe_qmat& m) { return moe::QMat{m.codes, m.scales, m.rows, m.
 // ---- workspace layouts -------------------------------------------------------
 size_t route_ws_bytes(int T, int E) { return align_up((size_t)T * E * sizeof(float)); }
 
-// fp32 activations: active-expert list + fp32 h.  bf16 activations: tile
-// list, block sums of x, and h as two bf16 planes (hi, then lo).
+// Expert-forward workspace: tile list, per-token row scales, the fp16
+// activation operand (hi plane; lo plane for fp32 activations) with its block
+// sums, and the intermediate h (hi, lo) with its block sums.  Block-sum rows
+// are padded to a multiple of 32 blocks.
+constexpr int kSmallTile = 16;
+
+int max_tiles(int T, int k, int E_local, int bm) {
+  const int64_t slots = (int64_t)T * k;
+  return (int)((slots + bm - 1) / bm + std::min<int64_t>(E_local, slots));
+}
+
+int pad32(int nb) { return (nb + 31) / 32 * 32; }
+
 struct FwdLayout {
-  size_t n_act, act, n_tiles, tiles, xs, h, total;
+  size_t n_tiles, tiles, sigma, xq_hi, xq_lo, sq_hi, sq_lo, h_hi, h_lo, hs_hi, hs_lo, total;
 };
 
-FwdLayout fwd_layout(int T, int H, int I, int k, int E, int E_local, int xt) {
+FwdLayout fwd_layout(int T, int H, int I, int k, int E_local, int xt) {
   FwdLayout L{};
+  const size_t TK = (size_t)T * k;
+  const size_t nb32H = pad32(H / 32), nb32I = pad32(I / 32);
   size_t off = 0;
-  L.n_act = off;
-  off += kAlign;
-  L.act = off;
-  off += align_up((size_t)E * sizeof(int32_t));
-  if (xt == MOE_ACT_BF16) {
-    L.n_tiles = off;
-    off += kAlign;
-    L.tiles = off;
-    off += align_up((size_t)moe::gemm_max_tiles(T, k, E_local) * 4 * sizeof(int32_t));
-    L.xs = off;
-    off += align_up((size_t)T * (H / 32) * sizeof(float));
-  }
-  L.h = off;
-  off += align_up((size_t)T * k * I * sizeof(float));
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  L.n_tiles = take(sizeof(int32_t));
+  L.tiles = take((size_t)max_tiles(T, k, E_local, kSmallTile) * 4 * sizeof(int32_t));
+  L.sigma = take((size_t)T * sizeof(float));
+  L.xq_hi = take((size_t)T * H * 2);
+  L.xq_lo = xt == MOE_ACT_F32 ? take((size_t)T * H * 2) : 0;
+  L.sq_hi = take((size_t)T * nb32H * 2);
+  L.sq_lo = take((size_t)T * nb32H * 2);
+  L.h_hi = take(TK * I * 2);
+  L.h_lo = take(TK * I * 2);
+  L.hs_hi = take(TK * nb32I * 2);
+  L.hs_lo = take(TK * nb32I * 2);
   L.total = off;
   return L;
 }
@@ -183,7 +198,7 @@ moe_status moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t k, int32_
   if (xt != MOE_ACT_F32 && xt != MOE_ACT_BF16) return fail(MOE_ERR_ARG, "moe_workspace_size: unknown activation type");
   if (route_ws) *route_ws = route_ws_bytes(T, E);
   if (group_ws) *group_ws = 0;
-  if (forward_ws) *forward_ws = fwd_layout(T, H, I, k, E, E_local, xt).total;
+  if (forward_ws) *forward_ws = fwd_layout(T, H, I, k, E_local, xt).total;
   return ok();
 }
 
@@ -282,15 +297,7 @@ moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, i
     return fail(MOE_ERR_ARG, "moe_expert_forward: NULL x, counts, offsets, slot_list or y_slot");
   if (!aligned16(x) || !aligned16(y_slot))
     return fail(MOE_ERR_ARG, "moe_expert_forward: x and y_slot must be 16-byte aligned");
-  if (xt == MOE_ACT_BF16) {
-    if (H % 64 || I % 64)
-      return fail(MOE_ERR_UNSUPPORTED, "moe_expert_forward: bf16 activations need H and I multiples of 64 (H = %d, I = %d)",
-                  H, I);
-    if (local->gate.fmt != MOE_W_Q2SM || local->down.fmt != MOE_W_Q8_0)
-      return fail(MOE_ERR_UNSUPPORTED,
-                  "moe_expert_forward: bf16 activations run Q2SM gate/up with a Q8_0 down projection");
-  }
-  const FwdLayout L = fwd_layout(T, H, I, k, E, E_local, xt);
+  const FwdLayout L = fwd_layout(T, H, I, k, E_local, xt);
   if (ws_bytes < L.total || !ws)
     return fail(MOE_ERR_WORKSPACE, "moe_expert_forward: workspace %zu bytes, need %zu", ws_bytes, L.total);
   if (T == 0) return ok();
@@ -312,26 +319,38 @@ moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, i
   if (dc.st) return dc.st;
 
   char* wsb = reinterpret_cast<char*>(ws);
-  if (xt == MOE_ACT_BF16) {
-    uint16_t* h_hi = reinterpret_cast<uint16_t*>(wsb + L.h);
-    uint16_t* h_lo = h_hi + (size_t)T * k * I;
-    hipError_t e = moe::launch_gemm_forward(
-        reinterpret_cast<const uint16_t*>(x), T, H, I, k, qm(local->gate), qm(local->up), qm(local->down), g2l, E,
-        E_local, counts, offsets, slot_list, reinterpret_cast<float*>(wsb + L.xs), reinterpret_cast<int4*>(wsb + L.tiles),
-        reinterpret_cast<int32_t*>(wsb + L.n_tiles), h_hi, h_lo, y_slot, s);
-    if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: GEMM launch");
-    return ok();
-  }
-  int32_t* n_act = reinterpret_cast<int32_t*>(wsb + L.n_act);
-  int32_t* act = reinterpret_cast<int32_t*>(wsb + L.act);
-  float* h = reinterpret_cast<float*>(wsb + L.h);
-  const int max_active = (int)std::min<int64_t>(E_local, (int64_t)T * k);
-  hipError_t e = moe::launch_active(counts, g2l, E, E_local, act, n_act, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: active-expert launch");
-  e = moe::launch_gemv_forward(reinterpret_cast<const float*>(x), T, H, I, k, qm(local->gate), qm(local->up),
-                               local->gate.fmt, qm(local->down), local->down.fmt, g2l, offsets, slot_list, act,
-                               n_act, max_active, h, y_slot, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: GEMV launch");
+  auto at16 = [&](size_t o) { return reinterpret_cast<uint16_t*>(wsb + o); };
+  moe::FfnArgs a{};
+  a.T = T; a.H = H; a.I = I; a.k = k;
+  a.fg = local->gate.fmt;
+  a.fd = local->down.fmt;
+  a.nb32H = pad32(H / 32);
+  a.nb32I = pad32(I / 32);
+  a.max_tiles = max_tiles(T, k, E_local, kSmallTile);
+  a.gate = qm(local->gate);
+  a.up = qm(local->up);
+  a.down = qm(local->down);
+  a.slot_list = slot_list;
+  a.tiles = reinterpret_cast<const int4*>(wsb + L.tiles);
+  a.n_tiles = reinterpret_cast<const int32_t*>(wsb + L.n_tiles);
+  a.xq_hi = at16(L.xq_hi);
+  a.xq_lo = xt == MOE_ACT_F32 ? at16(L.xq_lo) : nullptr;
+  a.sq_hi = at16(L.sq_hi);
+  a.sq_lo = at16(L.sq_lo);
+  a.sigma = reinterpret_cast<const float*>(wsb + L.sigma);
+  a.h_hi = at16(L.h_hi);
+  a.h_lo = at16(L.h_lo);
+  a.hs_hi = at16(L.hs_hi);
+  a.hs_lo = at16(L.hs_lo);
+  a.y = y_slot;
+  hipError_t e = moe::launch_prep(x, xt, a.fg, T, H, a.nb32H, at16(L.xq_hi), xt == MOE_ACT_F32 ? at16(L.xq_lo) : nullptr,
+                                  at16(L.sq_hi), at16(L.sq_lo), reinterpret_cast<float*>(wsb + L.sigma), counts,
+                                  offsets, g2l, E, E_local, T * k, kSmallTile, a.max_tiles,
+                                  reinterpret_cast<int4*>(wsb + L.tiles), reinterpret_cast<int32_t*>(wsb + L.n_tiles), s);
+  if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: prep launch");
+  const int nt_cols = (T >= 2 && H % 64 == 0 && I % 64 == 0) ? 4 : 2;
+  e = moe::launch_ffn_small(a, nt_cols, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: FFN launch");
   return ok();
 }
 
@@ -361,11 +380,11 @@ moe_status moe_combine(const float* y_slot, const float* w, const int32_t* ids, 
 moe_status moe_planar_bytes(int32_t fmt, int32_t rows, int32_t cols, size_t* codes_bytes, size_t* scales_bytes) {
   if (rows < 0 || cols <= 0 || cols % 32) return fail(MOE_ERR_ARG, "moe_planar_bytes: bad shape %dx%d", rows, cols);
   size_t c, sc;
-  const size_t nb = (size_t)rows * (cols / 32);
+  const size_t nb = (size_t)(cols / 32);
   switch (fmt) {
     case MOE_W_F32: c = (size_t)rows * cols * 4; sc = 0; break;
-    case MOE_W_Q8_0: c = (size_t)rows * cols; sc = nb * 2; break;
-    case MOE_W_Q2SM: c = (size_t)rows * cols / 4; sc = nb * 4; break;
+    case MOE_W_Q8_0: c = (size_t)rows * ((nb + 1) / 2) * 64; sc = (size_t)rows * nb * 2; break;
+    case MOE_W_Q2SM: c = (size_t)rows * ((nb + 7) / 8) * 64; sc = (size_t)rows * nb * 4; break;
     default: return fail(MOE_ERR_UNSUPPORTED, "moe_planar_bytes: unknown format %d", fmt);
   }
   if (codes_bytes) *codes_bytes = c;
@@ -373,31 +392,50 @@ moe_status moe_planar_bytes(int32_t fmt, int32_t rows, int32_t cols, size_t* cod
   return ok();
 }
 
+// Re-lay definition blocks into the unit layout documented in moe.h.
 moe_status moe_pack_planar(int32_t fmt, int32_t n, int32_t rows, int32_t cols, const void* aos, void* codes,
                            void* scales) {
   if (n < 0 || rows < 0 || cols <= 0 || cols % 32) return fail(MOE_ERR_ARG, "moe_pack_planar: bad shape");
   if (!aos || !codes || (fmt != MOE_W_F32 && !scales)) return fail(MOE_ERR_ARG, "moe_pack_planar: NULL pointer");
   const int64_t nb = cols / 32;
-  const int64_t blocks = (int64_t)n * rows * nb;
+  const int64_t nrows = (int64_t)n * rows;
   const uint8_t* src = static_cast<const uint8_t*>(aos);
   uint8_t* dc = static_cast<uint8_t*>(codes);
   uint8_t* ds = static_cast<uint8_t*>(scales);
   switch (fmt) {
     case MOE_W_F32:
-      std::memcpy(dc, src, (size_t)blocks * 128);
+      std::memcpy(dc, src, (size_t)nrows * cols * 4);
       break;
-    case MOE_W_Q8_0:
-      for (int64_t b = 0; b < blocks; ++b) {
-        std::memcpy(ds + 2 * b, src + 34 * b, 2);
-        std::memcpy(dc + 32 * b, src + 34 * b + 2, 32);
+    case MOE_W_Q8_0: {
+      const int64_t rb = (nb + 1) / 2 * 64;
+      std::memset(dc, 0, (size_t)(nrows * rb));
+      for (int64_t r = 0; r < nrows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+          const uint8_t* blk = src + (r * nb + b) * 34;
+          std::memcpy(ds + 2 * (r * nb + b), blk, 2);
+          for (int g = 0; g < 4; ++g)
+            std::memcpy(dc + r * rb + (b / 2) * 64 + g * 16 + (b % 2) * 8, blk + 2 + 8 * g, 8);
+        }
       }
       break;
-    case MOE_W_Q2SM:
-      for (int64_t b = 0; b < blocks; ++b) {
-        std::memcpy(ds + 4 * b, src + 12 * b, 4);
-        std::memcpy(dc + 8 * b, src + 12 * b + 4, 8);
+    }
+    case MOE_W_Q2SM: {
+      const int64_t rb = (nb + 7) / 8 * 64;
+      std::memset(dc, 0, (size_t)(nrows * rb));
+      for (int64_t r = 0; r < nrows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+          const uint8_t* blk = src + (r * nb + b) * 12;
+          std::memcpy(ds + 4 * (r * nb + b), blk, 4);
+          const int64_t i = (b % 8) / 2, h = b % 2;
+          for (int g = 0; g < 4; ++g) {
+            uint8_t* w = dc + r * rb + (b / 8) * 64 + g * 16 + i * 4;
+            w[h] = blk[4 + 2 * g];
+            w[2 + h] = blk[4 + 2 * g + 1];
+          }
+        }
       }
       break;
+    }
     default:
       return fail(MOE_ERR_UNSUPPORTED, "moe_pack_planar: unknown format %d", fmt);
   }

@@ -1,0 +1,138 @@
+// Device-side view of the quantised weight layouts and of the fp16 operands
+// the expert kernels feed to the matrix cores (internal to libmoe).
+//
+// Every expert matrix product runs on v_mfma_f32_16x16x32_f16, one
+// instruction per 32-value block, with the block's codes as the B operand.
+// A code enters the matrix core as an exact small fp16 integer: OR-ing a 2-bit
+// code q, shifted to bits p..p+1, into the mantissa of 1024.0 gives
+// 1024 + q*2^p, and one packed fp16 subtraction of 1024 leaves q*2^p; an 8-bit
+// code stored as u = q + 128 gives 1024 + u, and subtracting 1152 leaves q.
+// (Codes placed directly as fp16 subnormals would need no subtraction, but the
+// matrix cores then keep only about 17 significant bits of the block sum.)
+// The activation operand is prepared to match: value i of a block sits at the
+// K position its code occupies, multiplied by 2^(6-p) so that every product
+// carries the same factor 2^6, and by a per-row power-of-two sigma that keeps
+// it in fp16 range.  An fp32 activation is carried as two fp16 planes (hi + lo,
+// 22 significant bits).  Hence, for each block b of 32 values,
+//     P_b = sum_i A'_i B_i = 2^6 * sigma * sum_i q_i a_i
+// and the layer's value  sum_b sum_i (d_b q_i + m_b) a_i  is assembled as
+//     sigma * value = sum_b (2^-6 d_b) P_b  +  sum_b m_b (sigma S_b),
+// the second sum (S_b = block sum of a; Q2SM only, Q8_0 has m = 0) being one
+// more small matrix product over the block index.
+
+// Planar code layouts (bytes of the definition blocks, re-laid so that the
+// lane with K-group g of a 16x16x32 fragment reads exactly its own codes with
+// one 16-byte load; g covers values 8g..8g+7 of each block):
+//   Q2SM: a row is a sequence of 64-byte units of 8 blocks; in unit j the 16
+//         bytes of group g are 4 words, word i = [blk 2i byte 2g, blk 2i+1
+//         byte 2g, blk 2i byte 2g+1, blk 2i+1 byte 2g+1] (blk = block 8j+..).
+//   Q8_0: a row is a sequence of 64-byte units of 2 blocks; in unit j the 16
+//         bytes of group g are [blk 2j q[8g..8g+7], blk 2j+1 q[8g..8g+7]].
+//   Missing blocks of a row's last unit are zero.
+#pragma once
+#include "device.h"
+
+namespace moe {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t f16_bits(float v) {
+  _Float16 h = (_Float16)v;
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+// hi = v rounded to fp16, lo = (v - hi) rounded to fp16
+__device__ __forceinline__ void split_f16(float v, uint32_t& hi, uint32_t& lo) {
+  const _Float16 h = (_Float16)v;
+  hi = (uint32_t)__builtin_bit_cast(uint16_t, h);
+  lo = f16_bits(v - (float)h);
+}
+
+constexpr float kScaleD = 0.015625f;  // 2^-6: the block scale's factor against P_b
+constexpr float kSigmaH = 0.015625f;  // 2^-6: row scale of the intermediate h
+
+template <int FMT>
+struct Codes;
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// 1024 + v in each half (v < 1024) -> v, exactly
+__device__ __forceinline__ uint32_t sub_f16x2(uint32_t w, uint32_t neg_pair) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, w) + __builtin_bit_cast(f16x2_t, neg_pair));
+}
+
+template <>
+struct Codes<FMT_Q2SM> {
+  static constexpr int kUnitBlocks = 8;
+  static constexpr bool kHasM = true;
+  __host__ __device__ static constexpr int64_t row_bytes(int cols) { return (int64_t)((cols / 32 + 7) / 8) * 64; }
+  // B fragment of block i (0..7) of a unit from the lane's 16-byte chunk
+  __device__ static __forceinline__ uint4 frag(const uint4& c, int i) {
+    const uint32_t w = (i >> 1) == 0 ? c.x : (i >> 1) == 1 ? c.y : (i >> 1) == 2 ? c.z : c.w;
+    const uint32_t v = (i & 1) ? (w >> 8) : w;
+    constexpr uint32_t k1024 = 0x64006400u, kNeg1024 = 0xE400E400u;
+    return make_uint4(sub_f16x2((v & 0x00030003u) | k1024, kNeg1024), sub_f16x2((v & 0x000C000Cu) | k1024, kNeg1024),
+                      sub_f16x2((v & 0x00300030u) | k1024, kNeg1024), sub_f16x2((v & 0x00C000C0u) | k1024, kNeg1024));
+  }
+  // the block's d from the scale plane entry {d, m}
+  __device__ static __forceinline__ float d(const void* scales, int64_t idx) {
+    return half_bits_to_float(reinterpret_cast<const uint32_t*>(scales)[idx] & 0xFFFFu);
+  }
+  __device__ static __forceinline__ uint32_t m_bits(const void* scales, int64_t idx) {
+    return reinterpret_cast<const uint32_t*>(scales)[idx] >> 16;
+  }
+  // fragment element e (K position 8g+e) holds value 8g+val(e) at code bit position pos(e)
+  __host__ __device__ static constexpr int val(int e) { return (e >> 1) + 4 * (e & 1); }
+  __host__ __device__ static constexpr int pos(int e) { return 2 * (e >> 1); }
+  __host__ __device__ static constexpr int elem_of(int r) { return 2 * (r & 3) + (r >> 2); }  // inverse of val
+};
+
+template <>
+struct Codes<FMT_Q8_0> {
+  static constexpr int kUnitBlocks = 2;
+  static constexpr bool kHasM = false;
+  __host__ __device__ static constexpr int64_t row_bytes(int cols) { return (int64_t)((cols / 32 + 1) / 2) * 64; }
+  __device__ static __forceinline__ uint4 frag(const uint4& c, int i) {
+    const uint32_t a = (i ? c.z : c.x) ^ 0x80808080u;   // u = q + 128
+    const uint32_t b = (i ? c.w : c.y) ^ 0x80808080u;
+    constexpr uint32_t k64 = 0x64646464u, kNeg1152 = 0xE480E480u;
+    return make_uint4(sub_f16x2(__builtin_amdgcn_perm(k64, a, 0x04020400u), kNeg1152),
+                      sub_f16x2(__builtin_amdgcn_perm(k64, a, 0x04030401u), kNeg1152),
+                      sub_f16x2(__builtin_amdgcn_perm(k64, b, 0x04020400u), kNeg1152),
+                      sub_f16x2(__builtin_amdgcn_perm(k64, b, 0x04030401u), kNeg1152));
+  }
+  __device__ static __forceinline__ float d(const void* scales, int64_t idx) {
+    return half_bits_to_float(reinterpret_cast<const uint16_t*>(scales)[idx]);
+  }
+  __device__ static __forceinline__ uint32_t m_bits(const void*, int64_t) { return 0u; }
+  __host__ __device__ static constexpr int val(int e) { return (e == 1 || e == 5) ? e + 1 : (e == 2 || e == 6) ? e - 1 : e; }
+  __host__ __device__ static constexpr int pos(int) { return 0; }
+  __host__ __device__ static constexpr int elem_of(int r) { return val(r); }  // the order is an involution
+};
+
+// Runtime-format versions (the down projection's format decides how the
+// intermediate h is laid out by the gate/up kernel).
+__device__ __forceinline__ int elem_of_rt(int fmt, int r) {
+  return fmt == FMT_Q2SM ? Codes<FMT_Q2SM>::elem_of(r) : Codes<FMT_Q8_0>::elem_of(r);
+}
+__device__ __forceinline__ int pos_rt(int fmt, int e) {
+  return fmt == FMT_Q2SM ? Codes<FMT_Q2SM>::pos(e) : 0;
+}
+
+// B fragment for the m-term product: the 8 values m[row][b0..b0+7] as fp16
+// (zero past the last block).
+template <int FMT>
+__device__ __forceinline__ uint4 m_frag(const void* scales, int64_t row_base, int b0, int nb) {
+  uint32_t h[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) h[j] = (b0 + j < nb) ? Codes<FMT>::m_bits(scales, row_base + b0 + j) : 0u;
+  return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+}
+
+}  // namespace moe

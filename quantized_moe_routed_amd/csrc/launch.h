@@ -21,20 +21,28 @@ hipError_t launch_group(const int32_t* ids, int T, int k, int E, int32_t* counts
 size_t group_lds_bytes(int E);
 hipError_t group_set_lds_limit(size_t bytes);
 
-hipError_t launch_active(const int32_t* counts, const int32_t* g2l, int E, int E_local, int32_t* act,
-                         int32_t* n_act, hipStream_t s);
+// Arguments of the expert FFN launches (workspace pointers included).
+struct FfnArgs {
+  int T, H, I, k, fg, fd, nb32H, nb32I, max_tiles;
+  QMat gate, up, down;
+  const int32_t* slot_list;
+  const int4* tiles;
+  const int32_t* n_tiles;
+  const uint16_t *xq_hi, *xq_lo, *sq_hi, *sq_lo;
+  const float* sigma;
+  uint16_t *h_hi, *h_lo, *hs_hi, *hs_lo;
+  float* y;
+};
 
-hipError_t launch_gemv_forward(const float* x, int T, int H, int I, int k, const QMat& gate, const QMat& up,
-                               int gate_fmt, const QMat& down, int down_fmt, const int32_t* g2l,
-                               const int32_t* offsets, const int32_t* slot_list, const int32_t* act,
-                               const int32_t* n_act, int max_active, float* h_ws, float* y, hipStream_t s);
+// Tile list + fp16 activation operand (fmt.h) in one launch.
+hipError_t launch_prep(const void* x, int act, int fmt, int T, int H, int nb32, uint16_t* xq_hi, uint16_t* xq_lo,
+                       uint16_t* sq_hi, uint16_t* sq_lo, float* sigma, const int32_t* counts,
+                       const int32_t* offsets, const int32_t* g2l, int E, int E_local, int n_slots, int bm,
+                       int max_tiles, int4* tiles, int32_t* n_tiles, hipStream_t s);
 
-// Grouped MFMA GEMM (bf16 activations).  H and I must be multiples of 64.
-int gemm_max_tiles(int T, int k, int E_local);
-hipError_t launch_gemm_forward(const uint16_t* x, int T, int H, int I, int k, const QMat& gate, const QMat& up,
-                               const QMat& down, const int32_t* g2l, int E, int E_local, const int32_t* counts,
-                               const int32_t* offsets, const int32_t* slot_list, float* xs, int4* tiles,
-                               int32_t* n_tiles, uint16_t* h_hi, uint16_t* h_lo, float* y, hipStream_t s);
+// gate/up then down on tiles of up to 16 slots; nt_cols = 2 or 4 (output
+// columns per workgroup / 16).
+hipError_t launch_ffn_small(const FfnArgs& a, int nt_cols, hipStream_t s);
 
 hipError_t launch_combine(const float* y, const float* w, const int32_t* ids, const int32_t* g2l, int T, int k,
                           int H, int E, float* out, hipStream_t s);

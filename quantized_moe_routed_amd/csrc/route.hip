@@ -39,10 +39,16 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
     dsc[j] = 0.0f;
     if (b < nb) {
       if constexpr (FMT == FMT_Q8_0) {
-        const int8_t* q = reinterpret_cast<const int8_t*>(codes) + (int64_t)e * H + b * 32;
-        const int4* q4 = reinterpret_cast<const int4*>(q);
-        int4 a0 = q4[0], a1 = q4[1];
-        int words[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        // unit layout: block b's values 8g..8g+7 at unit b/2, group g, half b%2
+        const int8_t* q = reinterpret_cast<const int8_t*>(codes) + (int64_t)e * ((nb + 1) / 2) * 64 +
+                          (b >> 1) * 64 + (b & 1) * 8;
+        int words[8];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int2 v = *reinterpret_cast<const int2*>(q + 16 * g);
+          words[2 * g] = v.x;
+          words[2 * g + 1] = v.y;
+        }
 #pragma unroll
         for (int i = 0; i < 32; ++i) wv[j][i] = (float)(int8_t)(words[i / 4] >> (8 * (i % 4)));
         dsc[j] = half_bits_to_float(reinterpret_cast<const uint16_t*>(scales)[(int64_t)e * nb + b]);

@@ -31,26 +31,55 @@ def test_version():
     assert moe.version().startswith("moe-gfx950")
 
 
-@pytest.mark.parametrize("fmt,rows,cols", [(1, 3, 64), (2, 5, 96), (0, 2, 32)])
-def test_pack_planar_is_the_documented_permutation(fmt, rows, cols):
+def decode_planar(fmt, codes, scales, n, rows, cols):
+    """Values of n planar matrices, decoded from the unit layout as include/moe.h documents it."""
+    nb = cols // 32
+    out = np.zeros((n * rows, cols))
+    if fmt == 0:
+        return codes.view(np.float32).astype(np.float64).reshape(n * rows, cols)
+    if fmt == 1:
+        rb = (nb + 1) // 2 * 64
+        c = codes.reshape(n * rows, rb)
+        d = scales.view(np.float16).astype(np.float64).reshape(n * rows, nb)
+        for b in range(nb):
+            for g in range(4):
+                o = (b // 2) * 64 + g * 16 + (b % 2) * 8
+                q = c[:, o:o + 8].view(np.int8).astype(np.float64)
+                out[:, 32 * b + 8 * g:32 * b + 8 * g + 8] = d[:, b:b + 1] * q
+        return out
+    rb = (nb + 7) // 8 * 64
+    c = codes.reshape(n * rows, rb)
+    dm = scales.view(np.float16).astype(np.float64).reshape(n * rows, nb, 2)
+    for b in range(nb):
+        i, h = (b % 8) // 2, b % 2
+        for g in range(4):
+            w = (b // 8) * 64 + g * 16 + i * 4
+            lo_byte, hi_byte = c[:, w + h], c[:, w + 2 + h]        # definition bytes 2g and 2g+1
+            for s in range(4):
+                out[:, 32 * b + 8 * g + s] = dm[:, b, 0] * ((lo_byte >> (2 * s)) & 3) + dm[:, b, 1]
+                out[:, 32 * b + 8 * g + 4 + s] = dm[:, b, 0] * ((hi_byte >> (2 * s)) & 3) + dm[:, b, 1]
+    return out
+
+
+@pytest.mark.parametrize("fmt,rows,cols", [(1, 3, 64), (1, 2, 160), (2, 5, 96), (2, 3, 2080), (2, 2, 256),
+                                           (0, 2, 32)])
+def test_pack_planar_is_the_documented_unit_layout(fmt, rows, cols):
     aos = synth.quant_matrices(11, 77, 2, rows, cols, fmt)
     codes, scales = moe.pack_planar(fmt, aos, 2, rows, cols)
-    nb = cols // 32
-    if fmt == 0:
-        assert codes.tobytes() == aos.tobytes() and scales is None
-        return
-    bb = 34 if fmt == 1 else 12
-    blocks = aos.reshape(-1, bb)
-    hdr = 2 if fmt == 1 else 4
-    assert scales.tobytes() == blocks[:, :hdr].tobytes()
-    assert codes.tobytes() == blocks[:, hdr:].tobytes()
-    # planar code bytes keep the definition's bit order: value i of a row in byte i/4
-    if fmt == 2:
-        deq = oracle.dequant_rows(2, aos.reshape(-1, nb * 12), cols)
-        c = codes.reshape(-1, cols // 4)
-        d = np.frombuffer(scales.tobytes(), np.float16).reshape(-1, nb, 2).astype(np.float64)
-        q = np.stack([(c >> (2 * i)) & 3 for i in range(4)], -1).reshape(-1, nb, 32)
-        assert np.array_equal(d[..., 0:1] * q + d[..., 1:2], deq.reshape(-1, nb, 32))
+    cb, sb = moe.planar_bytes(fmt, rows, cols)
+    assert codes.size == 2 * cb and (scales is None) == (sb == 0)
+    got = decode_planar(fmt, codes, scales, 2, rows, cols)
+    ref = oracle.dequant_rows(fmt, aos.reshape(2 * rows, -1), cols)
+    assert np.array_equal(got, ref)
+    if fmt == 2 and (cols // 32) % 8:        # padding blocks of a row's last unit are zero
+        rb = (cols // 32 + 7) // 8 * 64
+        nb = cols // 32
+        c = codes.reshape(2 * rows, rb)
+        for b in range(nb, (nb + 7) // 8 * 8):
+            i, h = (b % 8) // 2, b % 2
+            for g in range(4):
+                w = (b // 8) * 64 + g * 16 + i * 4
+                assert not c[:, w + h].any() and not c[:, w + 2 + h].any()
 
 
 def test_lpt_matches_oracle():
@@ -162,15 +191,15 @@ def test_group_and_combine_argument_errors():
     moe.combine(FAKE, FAKE, FAKE, None, 0, 2, 256, 8, FAKE, stream=0)
 
 
-def test_bf16_forward_shape_and_format_limits():
+def test_bf16_forward_format_limits():
     big = 1 << 30
-    def call(H=256, I=128, gf=moe.W_Q2SM, df=moe.W_Q8_0):
+    def call(gf=moe.W_Q2SM, df=moe.W_Q8_0, H=256, I=128):
         ex = moe.Experts(moe.qmat(gf, I, H, FAKE, FAKE), moe.qmat(gf, I, H, FAKE, FAKE),
                          moe.qmat(df, H, I, FAKE, FAKE), 8)
         moe.expert_forward(FAKE, moe.ACT_BF16, 4, H, I, 2, ex, None, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, big, 0)
-    assert _status(lambda: call(H=160)) == moe.ERR_UNSUPPORTED          # H not a multiple of 64
-    assert _status(lambda: call(I=96)) == moe.ERR_UNSUPPORTED           # I not a multiple of 64
-    assert _status(lambda: call(gf=moe.W_Q8_0)) == moe.ERR_UNSUPPORTED  # MFMA path: Q2SM gate/up
-    assert _status(lambda: call(df=moe.W_Q2SM)) == moe.ERR_UNSUPPORTED  # MFMA path: Q8_0 down
+    assert _status(lambda: call(gf=moe.W_F32)) == moe.ERR_UNSUPPORTED
+    assert _status(lambda: call(df=moe.W_F32)) == moe.ERR_UNSUPPORTED
     a = moe.workspace_size(2048, 4096, 2048, 8, 256, 256, moe.ACT_BF16)
-    assert a[2] >= 2048 * 8 * 2048 * 4 + 2048 * 128 * 4
+    f = moe.workspace_size(2048, 4096, 2048, 8, 256, 256, moe.ACT_F32)
+    assert a[2] >= 2048 * 8 * 2048 * 4 + 2048 * 4096 * 2
+    assert f[2] == a[2] + 2048 * 4096 * 2       # fp32 activations add the lo plane
