@@ -77,11 +77,22 @@ typedef enum { MOE_W_F32 = 0, MOE_W_Q8_0 = 1, MOE_W_Q2SM = 2 } moe_wfmt;
 typedef enum { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 } moe_act;
 
 /* A stack of n matrices, each `rows` outputs x `cols` inputs, in the planar
- * device layout written by moe_pack_planar():
- *   F32  : codes = float  [n][rows][cols];                    scales = NULL
- *   Q8_0 : codes = int8   [n][rows][cols];                    scales = fp16 d      [n][rows][cols/32]
- *   Q2SM : codes = uint8  [n][rows][cols/4]  (value i of a row in byte i/4,
- *          bits 2*(i%4)..+1);                                  scales = fp16 {d,m}  [n][rows][cols/32][2]
+ * device layout written by moe_pack_planar() (sizes from moe_planar_bytes()).
+ * nb = cols/32 blocks per row.  Codes are cut into 64-byte units per row so
+ * that the lane that owns values 8g..8g+7 of a block (g = 0..3, the K-group of
+ * a 16x16x32 matrix-core fragment) reads exactly its codes with one 16-byte
+ * load:
+ *   F32  : codes = float [n][rows][cols];  scales = NULL.
+ *   Q8_0 : codes = [n][rows][ceil(nb/2)] units of 2 blocks; in unit j the 16
+ *          bytes at 16g are {block 2j q[8g..8g+7], block 2j+1 q[8g..8g+7]};
+ *          scales = fp16 d [n][rows][2*ceil(nb/2)].
+ *   Q2SM : codes = [n][rows][ceil(nb/8)] units of 8 blocks; in unit j the 16
+ *          bytes at 16g are 4 words, word i = {block 8j+2i byte 2g, block
+ *          8j+2i+1 byte 2g, block 8j+2i byte 2g+1, block 8j+2i+1 byte 2g+1},
+ *          where byte r of a block holds its values 4r..4r+3 (2 bits each,
+ *          value 4r+s at bits 2s..2s+1);
+ *          scales = per row, 8*ceil(nb/8) fp16 d values, then as many fp16 m.
+ * Blocks past nb (padding of a row's last unit) have zero codes and scales.
  * cols must be a multiple of 32. */
 typedef struct {
   int32_t fmt;
@@ -187,7 +198,8 @@ moe_status moe_planar_bytes(int32_t fmt, int32_t rows, int32_t cols, size_t* cod
 
 /* Re-lay n matrices from the definition layout (array of blocks: Q8_0
  * {fp16 d; int8 q[32]}, Q2SM {fp16 d; fp16 m; uint8 qs[8]}, F32 plain rows)
- * into the planar layout above.  Host memory in and out; a byte permutation. */
+ * into the planar layout above.  Host memory in and out; a byte permutation of
+ * the definition bytes plus zero padding. */
 moe_status moe_pack_planar(int32_t fmt, int32_t n, int32_t rows, int32_t cols, const void* aos,
                            void* codes, void* scales);
 

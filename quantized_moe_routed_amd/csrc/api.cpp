@@ -101,7 +101,7 @@ size_t route_ws_bytes(int T, int E) { return align_up((size_t)T * E * sizeof(flo
 // activation operand (hi plane; lo plane for fp32 activations) with its block
 // sums, and the intermediate h (hi, lo) with its block sums.  Block-sum rows
 // are padded to a multiple of 32 blocks.
-constexpr int kSmallTile = 16;
+constexpr int kSmallTile = 4;   // slots per tile of the expert kernels
 
 int max_tiles(int T, int k, int E_local, int bm) {
   const int64_t slots = (int64_t)T * k;
@@ -348,8 +348,7 @@ moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, i
                                   offsets, g2l, E, E_local, T * k, kSmallTile, a.max_tiles,
                                   reinterpret_cast<int4*>(wsb + L.tiles), reinterpret_cast<int32_t*>(wsb + L.n_tiles), s);
   if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: prep launch");
-  const int nt_cols = (T >= 2 && H % 64 == 0 && I % 64 == 0) ? 4 : 2;
-  e = moe::launch_ffn_small(a, nt_cols, s);
+  e = moe::launch_ffn_small(a, s);
   if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: FFN launch");
   return ok();
 }
@@ -383,8 +382,8 @@ moe_status moe_planar_bytes(int32_t fmt, int32_t rows, int32_t cols, size_t* cod
   const size_t nb = (size_t)(cols / 32);
   switch (fmt) {
     case MOE_W_F32: c = (size_t)rows * cols * 4; sc = 0; break;
-    case MOE_W_Q8_0: c = (size_t)rows * ((nb + 1) / 2) * 64; sc = (size_t)rows * nb * 2; break;
-    case MOE_W_Q2SM: c = (size_t)rows * ((nb + 7) / 8) * 64; sc = (size_t)rows * nb * 4; break;
+    case MOE_W_Q8_0: c = (size_t)rows * ((nb + 1) / 2) * 64; sc = (size_t)rows * ((nb + 1) / 2) * 4; break;
+    case MOE_W_Q2SM: c = (size_t)rows * ((nb + 7) / 8) * 64; sc = (size_t)rows * ((nb + 7) / 8) * 32; break;
     default: return fail(MOE_ERR_UNSUPPORTED, "moe_planar_bytes: unknown format %d", fmt);
   }
   if (codes_bytes) *codes_bytes = c;
@@ -407,12 +406,13 @@ moe_status moe_pack_planar(int32_t fmt, int32_t n, int32_t rows, int32_t cols, c
       std::memcpy(dc, src, (size_t)nrows * cols * 4);
       break;
     case MOE_W_Q8_0: {
-      const int64_t rb = (nb + 1) / 2 * 64;
+      const int64_t rb = (nb + 1) / 2 * 64, sb = (nb + 1) / 2 * 4;
       std::memset(dc, 0, (size_t)(nrows * rb));
+      std::memset(ds, 0, (size_t)(nrows * sb));
       for (int64_t r = 0; r < nrows; ++r) {
         for (int64_t b = 0; b < nb; ++b) {
           const uint8_t* blk = src + (r * nb + b) * 34;
-          std::memcpy(ds + 2 * (r * nb + b), blk, 2);
+          std::memcpy(ds + r * sb + 2 * b, blk, 2);
           for (int g = 0; g < 4; ++g)
             std::memcpy(dc + r * rb + (b / 2) * 64 + g * 16 + (b % 2) * 8, blk + 2 + 8 * g, 8);
         }
@@ -420,12 +420,14 @@ moe_status moe_pack_planar(int32_t fmt, int32_t n, int32_t rows, int32_t cols, c
       break;
     }
     case MOE_W_Q2SM: {
-      const int64_t rb = (nb + 7) / 8 * 64;
+      const int64_t rb = (nb + 7) / 8 * 64, nbp = (nb + 7) / 8 * 8;
       std::memset(dc, 0, (size_t)(nrows * rb));
+      std::memset(ds, 0, (size_t)(nrows * nbp * 4));
       for (int64_t r = 0; r < nrows; ++r) {
         for (int64_t b = 0; b < nb; ++b) {
           const uint8_t* blk = src + (r * nb + b) * 12;
-          std::memcpy(ds + 4 * (r * nb + b), blk, 4);
+          std::memcpy(ds + r * nbp * 4 + 2 * b, blk, 2);              // d row
+          std::memcpy(ds + r * nbp * 4 + 2 * (nbp + b), blk + 2, 2);  // m row
           const int64_t i = (b % 8) / 2, h = b % 2;
           for (int g = 0; g < 4; ++g) {
             uint8_t* w = dc + r * rb + (b / 8) * 64 + g * 16 + i * 4;

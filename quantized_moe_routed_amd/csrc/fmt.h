@@ -29,6 +29,9 @@
 //   Q8_0: a row is a sequence of 64-byte units of 2 blocks; in unit j the 16
 //         bytes of group g are [blk 2j q[8g..8g+7], blk 2j+1 q[8g..8g+7]].
 //   Missing blocks of a row's last unit are zero.
+// Planar scale layouts (one row per matrix row, padded to whole units, padding
+// zero): Q2SM: the unit-padded fp16 d values of the row, then its fp16 m
+// values; Q8_0: the unit-padded fp16 d values.
 #pragma once
 #include "device.h"
 
@@ -60,6 +63,20 @@ constexpr float kSigmaH = 0.015625f;  // 2^-6: row scale of the intermediate h
 template <int FMT>
 struct Codes;
 
+// Constants of the code unpacking, passed in from the host so that they live
+// in registers: VOP3 instructions (v_and_or_b32, v_perm_b32) take no literals
+// on this architecture.
+struct FragConsts {
+  uint32_t mask[4];      // 0x00030003 << 2s
+  uint32_t k1024;        // fp16 1024.0 in both halves
+  uint32_t neg1024;      // fp16 -1024.0 in both halves
+  uint32_t x80;          // 0x80808080
+  uint32_t k64;          // 0x64646464
+  uint32_t neg1152;      // fp16 -1152.0 in both halves
+  uint32_t sel_even;     // byte selectors {b0, 0x64, b2, 0x64} and {b1, 0x64, b3, 0x64}
+  uint32_t sel_odd;
+};
+
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // 1024 + v in each half (v < 1024) -> v, exactly
@@ -67,25 +84,31 @@ __device__ __forceinline__ uint32_t sub_f16x2(uint32_t w, uint32_t neg_pair) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, w) + __builtin_bit_cast(f16x2_t, neg_pair));
 }
 
+// A copy of a uniform value in a vector register, opaque to the optimiser.
+__device__ __forceinline__ uint32_t to_vgpr(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(v));
+  return r;
+}
+
+inline FragConsts frag_consts() {
+  return FragConsts{{0x00030003u, 0x000C000Cu, 0x00300030u, 0x00C000C0u}, 0x64006400u, 0xE400E400u, 0x80808080u,
+                    0x64646464u, 0xE480E480u, 0x04020400u, 0x04030401u};
+}
+
 template <>
 struct Codes<FMT_Q2SM> {
   static constexpr int kUnitBlocks = 8;
   static constexpr bool kHasM = true;
   __host__ __device__ static constexpr int64_t row_bytes(int cols) { return (int64_t)((cols / 32 + 7) / 8) * 64; }
+  __host__ __device__ static constexpr int64_t scale_row_bytes(int cols) { return (int64_t)((cols / 32 + 7) / 8) * 32; }
   // B fragment of block i (0..7) of a unit from the lane's 16-byte chunk
-  __device__ static __forceinline__ uint4 frag(const uint4& c, int i) {
+  // k1024v: fp16 1024.0 pairs held in a vector register (a VALU instruction reads one scalar register)
+  __device__ static __forceinline__ uint4 frag(const uint4& c, int i, const FragConsts& k, uint32_t k1024v) {
     const uint32_t w = (i >> 1) == 0 ? c.x : (i >> 1) == 1 ? c.y : (i >> 1) == 2 ? c.z : c.w;
     const uint32_t v = (i & 1) ? (w >> 8) : w;
-    constexpr uint32_t k1024 = 0x64006400u, kNeg1024 = 0xE400E400u;
-    return make_uint4(sub_f16x2((v & 0x00030003u) | k1024, kNeg1024), sub_f16x2((v & 0x000C000Cu) | k1024, kNeg1024),
-                      sub_f16x2((v & 0x00300030u) | k1024, kNeg1024), sub_f16x2((v & 0x00C000C0u) | k1024, kNeg1024));
-  }
-  // the block's d from the scale plane entry {d, m}
-  __device__ static __forceinline__ float d(const void* scales, int64_t idx) {
-    return half_bits_to_float(reinterpret_cast<const uint32_t*>(scales)[idx] & 0xFFFFu);
-  }
-  __device__ static __forceinline__ uint32_t m_bits(const void* scales, int64_t idx) {
-    return reinterpret_cast<const uint32_t*>(scales)[idx] >> 16;
+    return make_uint4(sub_f16x2((v & k.mask[0]) | k1024v, k.neg1024), sub_f16x2((v & k.mask[1]) | k1024v, k.neg1024),
+                      sub_f16x2((v & k.mask[2]) | k1024v, k.neg1024), sub_f16x2((v & k.mask[3]) | k1024v, k.neg1024));
   }
   // fragment element e (K position 8g+e) holds value 8g+val(e) at code bit position pos(e)
   __host__ __device__ static constexpr int val(int e) { return (e >> 1) + 4 * (e & 1); }
@@ -98,19 +121,15 @@ struct Codes<FMT_Q8_0> {
   static constexpr int kUnitBlocks = 2;
   static constexpr bool kHasM = false;
   __host__ __device__ static constexpr int64_t row_bytes(int cols) { return (int64_t)((cols / 32 + 1) / 2) * 64; }
-  __device__ static __forceinline__ uint4 frag(const uint4& c, int i) {
-    const uint32_t a = (i ? c.z : c.x) ^ 0x80808080u;   // u = q + 128
-    const uint32_t b = (i ? c.w : c.y) ^ 0x80808080u;
-    constexpr uint32_t k64 = 0x64646464u, kNeg1152 = 0xE480E480u;
-    return make_uint4(sub_f16x2(__builtin_amdgcn_perm(k64, a, 0x04020400u), kNeg1152),
-                      sub_f16x2(__builtin_amdgcn_perm(k64, a, 0x04030401u), kNeg1152),
-                      sub_f16x2(__builtin_amdgcn_perm(k64, b, 0x04020400u), kNeg1152),
-                      sub_f16x2(__builtin_amdgcn_perm(k64, b, 0x04030401u), kNeg1152));
+  __host__ __device__ static constexpr int64_t scale_row_bytes(int cols) { return (int64_t)((cols / 32 + 1) / 2) * 4; }
+  __device__ static __forceinline__ uint4 frag(const uint4& c, int i, const FragConsts& k, uint32_t) {
+    const uint32_t a = (i ? c.z : c.x) ^ k.x80;   // u = q + 128
+    const uint32_t b = (i ? c.w : c.y) ^ k.x80;
+    return make_uint4(sub_f16x2(__builtin_amdgcn_perm(k.k64, a, k.sel_even), k.neg1152),
+                      sub_f16x2(__builtin_amdgcn_perm(k.k64, a, k.sel_odd), k.neg1152),
+                      sub_f16x2(__builtin_amdgcn_perm(k.k64, b, k.sel_even), k.neg1152),
+                      sub_f16x2(__builtin_amdgcn_perm(k.k64, b, k.sel_odd), k.neg1152));
   }
-  __device__ static __forceinline__ float d(const void* scales, int64_t idx) {
-    return half_bits_to_float(reinterpret_cast<const uint16_t*>(scales)[idx]);
-  }
-  __device__ static __forceinline__ uint32_t m_bits(const void*, int64_t) { return 0u; }
   __host__ __device__ static constexpr int val(int e) { return (e == 1 || e == 5) ? e + 1 : (e == 2 || e == 6) ? e - 1 : e; }
   __host__ __device__ static constexpr int pos(int) { return 0; }
   __host__ __device__ static constexpr int elem_of(int r) { return val(r); }  // the order is an involution
@@ -123,16 +142,6 @@ __device__ __forceinline__ int elem_of_rt(int fmt, int r) {
 }
 __device__ __forceinline__ int pos_rt(int fmt, int e) {
   return fmt == FMT_Q2SM ? Codes<FMT_Q2SM>::pos(e) : 0;
-}
-
-// B fragment for the m-term product: the 8 values m[row][b0..b0+7] as fp16
-// (zero past the last block).
-template <int FMT>
-__device__ __forceinline__ uint4 m_frag(const void* scales, int64_t row_base, int b0, int nb) {
-  uint32_t h[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) h[j] = (b0 + j < nb) ? Codes<FMT>::m_bits(scales, row_base + b0 + j) : 0u;
-  return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
 }
 
 }  // namespace moe

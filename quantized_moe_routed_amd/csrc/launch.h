@@ -40,9 +40,8 @@ hipError_t launch_prep(const void* x, int act, int fmt, int T, int H, int nb32, 
                        const int32_t* offsets, const int32_t* g2l, int E, int E_local, int n_slots, int bm,
                        int max_tiles, int4* tiles, int32_t* n_tiles, hipStream_t s);
 
-// gate/up then down on tiles of up to 16 slots; nt_cols = 2 or 4 (output
-// columns per workgroup / 16).
-hipError_t launch_ffn_small(const FfnArgs& a, int nt_cols, hipStream_t s);
+// gate/up then down on tiles of up to 4 slots, 32 output columns per workgroup.
+hipError_t launch_ffn_small(const FfnArgs& a, hipStream_t s);
 
 hipError_t launch_combine(const float* y, const float* w, const int32_t* ids, const int32_t* g2l, int T, int k,
                           int H, int E, float* out, hipStream_t s);

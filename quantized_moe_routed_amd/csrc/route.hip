@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
         }
 #pragma unroll
         for (int i = 0; i < 32; ++i) wv[j][i] = (float)(int8_t)(words[i / 4] >> (8 * (i % 4)));
-        dsc[j] = half_bits_to_float(reinterpret_cast<const uint16_t*>(scales)[(int64_t)e * nb + b]);
+        dsc[j] = half_bits_to_float(reinterpret_cast<const uint16_t*>(scales)[(int64_t)e * ((nb + 1) / 2 * 2) + b]);
       } else {
         const float4* w4 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(codes) +
                                                            (int64_t)e * H + b * 32);

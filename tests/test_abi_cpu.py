@@ -40,7 +40,7 @@ def decode_planar(fmt, codes, scales, n, rows, cols):
     if fmt == 1:
         rb = (nb + 1) // 2 * 64
         c = codes.reshape(n * rows, rb)
-        d = scales.view(np.float16).astype(np.float64).reshape(n * rows, nb)
+        d = scales.view(np.float16).astype(np.float64).reshape(n * rows, (nb + 1) // 2 * 2)
         for b in range(nb):
             for g in range(4):
                 o = (b // 2) * 64 + g * 16 + (b % 2) * 8
@@ -48,8 +48,10 @@ def decode_planar(fmt, codes, scales, n, rows, cols):
                 out[:, 32 * b + 8 * g:32 * b + 8 * g + 8] = d[:, b:b + 1] * q
         return out
     rb = (nb + 7) // 8 * 64
+    nbp = (nb + 7) // 8 * 8
     c = codes.reshape(n * rows, rb)
-    dm = scales.view(np.float16).astype(np.float64).reshape(n * rows, nb, 2)
+    sc = scales.view(np.float16).astype(np.float64).reshape(n * rows, 2, nbp)   # d row, then m row
+    dm = np.stack([sc[:, 0, :nb], sc[:, 1, :nb]], -1)
     for b in range(nb):
         i, h = (b % 8) // 2, b % 2
         for g in range(4):
@@ -71,7 +73,11 @@ def test_pack_planar_is_the_documented_unit_layout(fmt, rows, cols):
     got = decode_planar(fmt, codes, scales, 2, rows, cols)
     ref = oracle.dequant_rows(fmt, aos.reshape(2 * rows, -1), cols)
     assert np.array_equal(got, ref)
-    if fmt == 2 and (cols // 32) % 8:        # padding blocks of a row's last unit are zero
+    if fmt == 1 and (cols // 32) % 2:        # scale padding is zero
+        assert not scales.view(np.uint16).reshape(2 * rows, -1)[:, -1].any()
+    if fmt == 2 and (cols // 32) % 8:        # padding blocks of a row's last unit are zero, codes and scales
+        sc = scales.view(np.uint16).reshape(2 * rows, 2, -1)
+        assert not sc[:, :, cols // 32:].any()
         rb = (cols // 32 + 7) // 8 * 64
         nb = cols // 32
         c = codes.reshape(2 * rows, rb)
