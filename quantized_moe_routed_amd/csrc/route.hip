@@ -124,61 +124,81 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
   }
 }
 
-// a ranks before b: larger z, then lower index; NaN ranks last.
-__device__ __forceinline__ bool ranks_before(float za, int a, float zb, int b) {
-  const bool na = za != za, nb = zb != zb;
-  if (na || nb) return (na != nb) ? nb : (a < b);
-  if (za != zb) return za > zb;
-  return a < b;
+// Order-preserving unsigned key of a logit: larger z -> larger key, -0 and +0
+// equal, NaN -> 0 (below every number).  key_to_float inverts it (0 -> NaN).
+__device__ __forceinline__ uint32_t float_key(float z) {
+  if (z != z) return 0u;
+  if (z == 0.0f) z = 0.0f;   // -0 -> +0
+  const uint32_t b = __float_as_uint(z);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// One wave per token: k rounds of a wave-wide arg-max over the unselected experts.
+// Wave-wide max / min of an unsigned value: quad and row permutes (DPP) reduce
+// each row of 16 lanes, then the four row results are read out.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+
+// One wave per token: k rounds, each a wave max of the logit key over the
+// untaken experts followed by a wave min of the expert index among those that
+// hold it (ties go to the lower index).  Weights: s_j = sigmoid(z_j) in fp64
+// on lane j, their sum taken in slot order by every lane, w_j = s_j / sum.
 template <int EPL>  // experts per lane (E <= 64 * EPL)
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ z, int T, int E, int k,
                                                          int32_t* __restrict__ ids, float* __restrict__ w) {
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
-  float zv[EPL];
-  bool taken[EPL];
+  uint32_t key[EPL];
+  bool live[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = i * kWave + lane;
-    taken[i] = e >= E;
-    zv[i] = e < E ? z[(int64_t)t * E + e] : 0.0f;
+    live[i] = e < E;
+    key[i] = live[i] ? float_key(z[(int64_t)t * E + e]) : 0u;
   }
-  // lane j keeps slot j's expert and sigmoid score; the sum is wave-uniform
-  double my_s = 0.0, ssum = 0.0;
   int my_id = -1;
+  uint32_t my_key = 0;
   for (int j = 0; j < k; ++j) {
-    float bz = 0.0f;
-    int be = -1;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = i * kWave + lane;
-      if (!taken[i] && (be < 0 || ranks_before(zv[i], e, bz, be))) {
-        bz = zv[i];
-        be = e;
-      }
-    }
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-      const float oz = __shfl_xor(bz, m, kWave);
-      const int oe = __shfl_xor(be, m, kWave);
-      if (oe >= 0 && (be < 0 || ranks_before(oz, oe, bz, be))) {
-        bz = oz;
-        be = oe;
-      }
-    }
+    uint32_t lk = 0;
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
-      if (i * kWave + lane == be) taken[i] = true;
-    const double sj = 1.0 / (1.0 + exp(-(double)bz));
-    ssum += sj;
-    if (lane == j) {
-      my_s = sj;
-      my_id = be;
+      if (live[i] && key[i] > lk) lk = key[i];
+    const uint32_t mk = wave_reduce_u32<true>(lk);
+    uint32_t li = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const uint32_t e = (uint32_t)(i * kWave + lane);
+      if (live[i] && key[i] == mk && e < li) li = e;
     }
+    const uint32_t me = wave_reduce_u32<false>(li);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if ((uint32_t)(i * kWave + lane) == me) live[i] = false;
+    if (lane == j) {
+      my_id = (int)me;
+      my_key = mk;
+    }
+  }
+  const double my_s = 1.0 / (1.0 + exp(-(double)key_to_float(my_key)));
+  double ssum = 0.0;
+  for (int j = 0; j < k; ++j) {
+    const int lo = __builtin_amdgcn_readlane((int)(uint32_t)__double_as_longlong(my_s), j);
+    const int hi = __builtin_amdgcn_readlane((int)(uint32_t)(__double_as_longlong(my_s) >> 32), j);
+    ssum += __longlong_as_double(((long long)(uint32_t)hi << 32) | (uint32_t)lo);
   }
   if (lane < k) {
     ids[(int64_t)t * k + lane] = my_id;
