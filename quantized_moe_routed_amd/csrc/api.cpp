@@ -101,31 +101,48 @@ size_t route_ws_bytes(int T, int E) { return align_up((size_t)T * E * sizeof(flo
 // activation operand (hi plane; lo plane for fp32 activations) with its block
 // sums, and the intermediate h (hi, lo) with its block sums.  Block-sum rows
 // are padded to a multiple of 32 blocks.
-constexpr int kSmallTile = 4;   // slots per tile of the expert kernels
+constexpr int kSmallTile = 4;     // slots per small tile of the expert kernels
+constexpr int kLargeTile = 128;   // slots per large tile
+constexpr int kLargeMin = 16;     // experts with at least this many slots use large tiles
 
-int max_tiles(int T, int k, int E_local, int bm) {
+int64_t max_tiles(int64_t slots, int64_t experts, int bm) { return (slots + bm - 1) / bm + experts; }
+
+// Tile-list bounds for T tokens (an expert receives at most T slots).
+struct TilePlan {
+  int large_min, max_small, max_large;
+};
+
+TilePlan tile_plan(int T, int H, int I, int k, int E_local) {
   const int64_t slots = (int64_t)T * k;
-  return (int)((slots + bm - 1) / bm + std::min<int64_t>(E_local, slots));
+  TilePlan p{};
+  const bool large = T >= kLargeMin && H % 64 == 0 && I % 64 == 0;
+  p.large_min = large ? kLargeMin : 0x7FFFFFFF;
+  p.max_small = (int)max_tiles(slots, std::min<int64_t>(E_local, slots), kSmallTile);
+  p.max_large = large ? (int)max_tiles(slots, std::min<int64_t>(E_local, slots / kLargeMin), kLargeTile) : 0;
+  return p;
 }
 
 int pad32(int nb) { return (nb + 31) / 32 * 32; }
 
 struct FwdLayout {
-  size_t n_tiles, tiles, sigma, xq_hi, xq_lo, sq_hi, sq_lo, h_hi, h_lo, hs_hi, hs_lo, total;
+  size_t n_small, n_large, small, large, sigma, xq_hi, xq_lo, sq_hi, sq_lo, h_hi, h_lo, hs_hi, hs_lo, total;
 };
 
 FwdLayout fwd_layout(int T, int H, int I, int k, int E_local, int xt) {
   FwdLayout L{};
   const size_t TK = (size_t)T * k;
   const size_t nb32H = pad32(H / 32), nb32I = pad32(I / 32);
+  const TilePlan tp = tile_plan(T, H, I, k, E_local);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off += align_up(bytes);
     return at;
   };
-  L.n_tiles = take(sizeof(int32_t));
-  L.tiles = take((size_t)max_tiles(T, k, E_local, kSmallTile) * 4 * sizeof(int32_t));
+  L.n_small = take(sizeof(int32_t));
+  L.n_large = take(sizeof(int32_t));
+  L.small = take((size_t)tp.max_small * 4 * sizeof(int32_t));
+  L.large = take((size_t)tp.max_large * 4 * sizeof(int32_t));
   L.sigma = take((size_t)T * sizeof(float));
   L.xq_hi = take((size_t)T * H * 2);
   L.xq_lo = xt == MOE_ACT_F32 ? take((size_t)T * H * 2) : 0;
@@ -321,18 +338,22 @@ moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, i
   char* wsb = reinterpret_cast<char*>(ws);
   auto at16 = [&](size_t o) { return reinterpret_cast<uint16_t*>(wsb + o); };
   moe::FfnArgs a{};
+  const TilePlan tp = tile_plan(T, H, I, k, E_local);
   a.T = T; a.H = H; a.I = I; a.k = k;
   a.fg = local->gate.fmt;
   a.fd = local->down.fmt;
   a.nb32H = pad32(H / 32);
   a.nb32I = pad32(I / 32);
-  a.max_tiles = max_tiles(T, k, E_local, kSmallTile);
   a.gate = qm(local->gate);
   a.up = qm(local->up);
   a.down = qm(local->down);
   a.slot_list = slot_list;
-  a.tiles = reinterpret_cast<const int4*>(wsb + L.tiles);
-  a.n_tiles = reinterpret_cast<const int32_t*>(wsb + L.n_tiles);
+  a.small = reinterpret_cast<const int4*>(wsb + L.small);
+  a.large = reinterpret_cast<const int4*>(wsb + L.large);
+  a.n_small = reinterpret_cast<const int32_t*>(wsb + L.n_small);
+  a.n_large = reinterpret_cast<const int32_t*>(wsb + L.n_large);
+  a.max_small = tp.max_small;
+  a.max_large = tp.max_large;
   a.xq_hi = at16(L.xq_hi);
   a.xq_lo = xt == MOE_ACT_F32 ? at16(L.xq_lo) : nullptr;
   a.sq_hi = at16(L.sq_hi);
@@ -343,12 +364,26 @@ moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, i
   a.hs_hi = at16(L.hs_hi);
   a.hs_lo = at16(L.hs_lo);
   a.y = y_slot;
+  moe::TileLists tl{};
+  tl.counts = counts;
+  tl.offsets = offsets;
+  tl.g2l = g2l;
+  tl.E = E;
+  tl.E_local = E_local;
+  tl.n_slots = T * k;
+  tl.large_min = tp.large_min;
+  tl.bm_small = kSmallTile;
+  tl.max_small = tp.max_small;
+  tl.bm_large = kLargeTile;
+  tl.max_large = tp.max_large;
+  tl.small = reinterpret_cast<int4*>(wsb + L.small);
+  tl.large = reinterpret_cast<int4*>(wsb + L.large);
+  tl.n_small = reinterpret_cast<int32_t*>(wsb + L.n_small);
+  tl.n_large = reinterpret_cast<int32_t*>(wsb + L.n_large);
   hipError_t e = moe::launch_prep(x, xt, a.fg, T, H, a.nb32H, at16(L.xq_hi), xt == MOE_ACT_F32 ? at16(L.xq_lo) : nullptr,
-                                  at16(L.sq_hi), at16(L.sq_lo), reinterpret_cast<float*>(wsb + L.sigma), counts,
-                                  offsets, g2l, E, E_local, T * k, kSmallTile, a.max_tiles,
-                                  reinterpret_cast<int4*>(wsb + L.tiles), reinterpret_cast<int32_t*>(wsb + L.n_tiles), s);
+                                  at16(L.sq_hi), at16(L.sq_lo), reinterpret_cast<float*>(wsb + L.sigma), tl, s);
   if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: prep launch");
-  e = moe::launch_ffn_small(a, s);
+  e = moe::launch_ffn(a, s);
   if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: FFN launch");
   return ok();
 }

@@ -21,27 +21,38 @@ hipError_t launch_group(const int32_t* ids, int T, int k, int E, int32_t* counts
 size_t group_lds_bytes(int E);
 hipError_t group_set_lds_limit(size_t bytes);
 
+// Two tile lists over the owned experts that received slots: experts with
+// fewer than large_min slots in tiles of bm_small, the others in tiles of
+// bm_large.  A tile is {local expert, first grouped position, rows, global id}.
+struct TileLists {
+  const int32_t *counts, *offsets, *g2l;
+  int E, E_local, n_slots, large_min;
+  int bm_small, max_small, bm_large, max_large;
+  int4 *small, *large;
+  int32_t *n_small, *n_large;
+};
+
 // Arguments of the expert FFN launches (workspace pointers included).
 struct FfnArgs {
-  int T, H, I, k, fg, fd, nb32H, nb32I, max_tiles;
+  int T, H, I, k, fg, fd, nb32H, nb32I;
   QMat gate, up, down;
   const int32_t* slot_list;
-  const int4* tiles;
-  const int32_t* n_tiles;
+  const int4 *small, *large;
+  const int32_t *n_small, *n_large;
+  int max_small, max_large;   // max_large = 0: no large tiles can exist
   const uint16_t *xq_hi, *xq_lo, *sq_hi, *sq_lo;
   const float* sigma;
   uint16_t *h_hi, *h_lo, *hs_hi, *hs_lo;
   float* y;
 };
 
-// Tile list + fp16 activation operand (fmt.h) in one launch.
+// Tile lists + fp16 activation operand (fmt.h) in one launch.
 hipError_t launch_prep(const void* x, int act, int fmt, int T, int H, int nb32, uint16_t* xq_hi, uint16_t* xq_lo,
-                       uint16_t* sq_hi, uint16_t* sq_lo, float* sigma, const int32_t* counts,
-                       const int32_t* offsets, const int32_t* g2l, int E, int E_local, int n_slots, int bm,
-                       int max_tiles, int4* tiles, int32_t* n_tiles, hipStream_t s);
+                       uint16_t* sq_hi, uint16_t* sq_lo, float* sigma, const TileLists& tl, hipStream_t s);
 
-// gate/up then down on tiles of up to 4 slots, 32 output columns per workgroup.
-hipError_t launch_ffn_small(const FfnArgs& a, hipStream_t s);
+// gate/up then down: small tiles (up to 4 slots, 32 output columns per
+// workgroup) and large tiles (up to 128 slots, 64 columns per workgroup).
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 
 hipError_t launch_combine(const float* y, const float* w, const int32_t* ids, const int32_t* g2l, int T, int k,
                           int H, int E, float* out, hipStream_t s);

@@ -22,17 +22,21 @@ __device__ __forceinline__ float act_at(const void* x, int64_t i) {
   return load_act<ACT>(x, i);
 }
 
+// Tiles of bm slots over the owned experts with lo_n <= slots < hi_n that
+// received slots, in ascending global id: tile i covers grouped positions
+// p0 .. p0+rows-1 of local expert .x.  Tiles past max_tiles, and rows past the
+// n_slots grouped positions, are never produced, whatever the counts hold.
 __device__ void build_tiles(const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-                            const int32_t* __restrict__ g2l, int E, int E_local, int n_slots, int bm,
-                            int max_tiles, int4* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
-  __shared__ int32_t wave_tot[kPrepThreads / kWave];
+                            const int32_t* __restrict__ g2l, int E, int E_local, int n_slots, int bm, int lo_n,
+                            int hi_n, int max_tiles, int4* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+                            int32_t* wave_tot) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   int n = 0, mt = 0, l = -1, p = 0;
   if (tid < E) {
     l = g2l ? g2l[tid] : tid;
     p = offsets[tid];
     n = (p >= 0 && p < n_slots) ? min(counts[tid], n_slots - p) : 0;
-    if (n > 0 && l >= 0 && l < E_local) mt = (n + bm - 1) / bm;
+    if (n > 0 && n >= lo_n && n < hi_n && l >= 0 && l < E_local) mt = (n + bm - 1) / bm;
   }
   int incl = mt;
 #pragma unroll
@@ -40,6 +44,7 @@ __device__ void build_tiles(const int32_t* __restrict__ counts, const int32_t* _
     const int o = __shfl_up(incl, d, kWave);
     if (lane >= d) incl += o;
   }
+  __syncthreads();   // wave_tot may still be read by an earlier call
   if (lane == kWave - 1) wave_tot[wave] = incl;
   __syncthreads();
   int base = 0;
@@ -110,13 +115,16 @@ __device__ void prep_token(const void* __restrict__ x, int t, int H, int nb32, u
 }
 
 template <int ACT, int FMT>
-__global__ __launch_bounds__(kPrepThreads) void prep_kernel(
-    const void* __restrict__ x, int T, int H, int nb32, uint16_t* __restrict__ xq_hi, uint16_t* __restrict__ xq_lo,
-    uint16_t* __restrict__ sq_hi, uint16_t* __restrict__ sq_lo, float* __restrict__ sigma,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, const int32_t* __restrict__ g2l, int E,
-    int E_local, int n_slots, int bm, int max_tiles, int4* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(const void* __restrict__ x, int T, int H, int nb32,
+                                                            uint16_t* __restrict__ xq_hi, uint16_t* __restrict__ xq_lo,
+                                                            uint16_t* __restrict__ sq_hi, uint16_t* __restrict__ sq_lo,
+                                                            float* __restrict__ sigma, TileLists tl) {
+  __shared__ int32_t wave_tot[kPrepThreads / kWave];
   if (blockIdx.x == 0) {
-    build_tiles(counts, offsets, g2l, E, E_local, n_slots, bm, max_tiles, tiles, n_tiles);
+    build_tiles(tl.counts, tl.offsets, tl.g2l, tl.E, tl.E_local, tl.n_slots, tl.bm_small, 1, tl.large_min,
+                tl.max_small, tl.small, tl.n_small, wave_tot);
+    build_tiles(tl.counts, tl.offsets, tl.g2l, tl.E, tl.E_local, tl.n_slots, tl.bm_large, tl.large_min, 0x7FFFFFFF,
+                tl.max_large, tl.large, tl.n_large, wave_tot);
   } else {
     const int t = blockIdx.x - 1;
     if (t < T) prep_token<ACT, FMT>(x, t, H, nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma);
@@ -124,14 +132,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
 }
 
 hipError_t launch_prep(const void* x, int act, int fmt, int T, int H, int nb32, uint16_t* xq_hi, uint16_t* xq_lo,
-                       uint16_t* sq_hi, uint16_t* sq_lo, float* sigma, const int32_t* counts,
-                       const int32_t* offsets, const int32_t* g2l, int E, int E_local, int n_slots, int bm,
-                       int max_tiles, int4* tiles, int32_t* n_tiles, hipStream_t s) {
+                       uint16_t* sq_hi, uint16_t* sq_lo, float* sigma, const TileLists& tl, hipStream_t s) {
   const dim3 grid(1 + T);
   trace_pre("prep", s);
-#define MOE_PREP(A, F)                                                                                            \
-  prep_kernel<A, F><<<grid, kPrepThreads, 0, s>>>(x, T, H, nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma, counts,      \
-                                                  offsets, g2l, E, E_local, n_slots, bm, max_tiles, tiles, n_tiles)
+#define MOE_PREP(A, F) \
+  prep_kernel<A, F><<<grid, kPrepThreads, 0, s>>>(x, T, H, nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma, tl)
   if (act == ACT_F32) {
     if (fmt == FMT_Q2SM) MOE_PREP(ACT_F32, FMT_Q2SM);
     else MOE_PREP(ACT_F32, FMT_Q8_0);

@@ -226,3 +226,30 @@ def test_bf16_small_shapes_and_share(torch):
         check_against_oracle(wl, gs, oracle_expect(wl, l2g=l2g, g2l=g2l), what=f"bf16 share {share}")
         parts.append(gs["out"].astype(np.float64))
     assert_close(parts[0] + parts[1], got["out"], "bf16 share A + share B vs full")
+
+
+# ---- large tiles: experts with 16 or more slots --------------------------------------------
+
+_LARGE_CASES = {
+    # fp32 activations (hi + lo planes), 2-bit everywhere, a partly filled last code unit (H = 320)
+    "f32_q2sm": (64, 320, 8, 192, 2, dict(gate_fmt=2, up_fmt=2, down_fmt=2, router_fmt=1, act="f32")),
+    # fp32 activations, Q8_0 everywhere, fp32 router
+    "f32_q8": (64, 256, 6, 320, 2, dict(gate_fmt=1, up_fmt=1, down_fmt=1, router_fmt=0, act="f32")),
+    # bf16 activations, Q8_0 gate/up, 2-bit down
+    "bf16_q8_q2sm": (48, 192, 8, 256, 3, dict(gate_fmt=1, up_fmt=1, down_fmt=2, router_fmt=1, act="bf16")),
+    # several full tiles of 128 slots per expert plus ragged tails, next to one small expert
+    "f32_multi_tile": (300, 128, 4, 128, 2, dict(gate_fmt=2, up_fmt=2, down_fmt=1, router_fmt=1, act="f32")),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_LARGE_CASES))
+def test_large_tiles_against_oracle(torch, name):
+    T, H, E, I, k, kw = _LARGE_CASES[name]
+    _say(f"large tiles {name}: T={T} H={H} E={E} I={I} k={k}")
+    wl = synth.make(synth.custom(T, H, E, I, k, bias="zipf1.1", name=name, **kw))
+    got = run(make_layer(wl), wl, torch)
+    counts = got["counts"]
+    assert counts.max() >= 16 and ((counts > 0) & (counts < 16)).any()   # both tile kinds in use
+    if name == "f32_multi_tile":
+        assert counts.max() > 2 * 128
+    check_against_oracle(wl, got, oracle_expect(wl), what=f"large {name}")
