@@ -23,6 +23,7 @@ SOURCES = {
     "group.hip": [],
     "prep.hip": [],
     "ffn.hip": [],
+    "ffn_large.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "combine.hip": [],
     "api.cpp": [],
 }

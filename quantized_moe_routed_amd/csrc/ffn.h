@@ -1,0 +1,50 @@
+// Shared pieces of the two expert-FFN kernels (internal to libmoe): the
+// argument block of one projection launch and the block-scale accessors.
+#pragma once
+#include "device.h"
+#include "fmt.h"
+
+namespace moe {
+
+enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
+
+struct FfnTileArgs {
+  const uint16_t *a_hi, *a_lo;      // activation operand planes, row stride K
+  const uint16_t *s_hi, *s_lo;      // block-sum planes, row stride nb32
+  const float* sigma;               // per-token row scale (gate/up); NULL: kSigmaH (down)
+  int K, N, nb32, k;
+  QMat w0, w1;                      // gate, up (gate/up) or down (w0 only)
+  const int32_t* slot_list;
+  const int4* tiles;
+  const int32_t* n_tiles;
+  int fd, I, nb32I;                 // gate/up: down format, I, padded block count of h
+  int stage_rows;                   // small tiles: rows of the LDS staging area (min(4, T))
+  FragConsts kc;
+  uint16_t *h_hi, *h_lo, *hs_hi, *hs_lo;
+  float* y;
+};
+
+template <int F>
+__device__ __forceinline__ uint4 load_d(const uint8_t* srow, int u) {
+  if constexpr (F == FMT_Q2SM) {
+    return *reinterpret_cast<const uint4*>(srow + 16 * (int64_t)u);
+  } else {
+    return make_uint4(*reinterpret_cast<const uint32_t*>(srow + 4 * (int64_t)u), 0u, 0u, 0u);
+  }
+}
+
+template <int F>
+__device__ __forceinline__ float d_of(const uint4& dw, int i) {
+  uint32_t w;
+  if constexpr (F == FMT_Q2SM) {
+    w = (i >> 1) == 0 ? dw.x : (i >> 1) == 1 ? dw.y : (i >> 1) == 2 ? dw.z : dw.w;
+  } else {
+    w = dw.x;
+  }
+  return half_bits_to_float((i & 1) ? (w >> 16) : (w & 0xFFFFu)) * kScaleD;
+}
+
+// Large-tile launch (ffn_large.hip): tiles of up to 128 slots of one expert.
+hipError_t launch_large(const FfnTileArgs& t, int fmt, int mode, bool lo, int max_tiles, hipStream_t s);
+
+}  // namespace moe

@@ -26,6 +26,7 @@
 #include "device.h"
 #include "fmt.h"
 #include "launch.h"
+#include "ffn.h"
 
 namespace moe {
 
@@ -33,44 +34,6 @@ constexpr int kFfnThreads = 512;
 constexpr int kFfnWaves = kFfnThreads / 64;
 constexpr int kNT = 2;            // 16-column output tiles per workgroup
 constexpr int kStageRows = 4;     // slots per tile; their activation rows are staged in LDS
-
-enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
-
-struct FfnTileArgs {
-  const uint16_t *a_hi, *a_lo;      // activation operand planes, row stride K
-  const uint16_t *s_hi, *s_lo;      // block-sum planes, row stride nb32
-  const float* sigma;               // per-token row scale (gate/up); NULL: kSigmaH (down)
-  int K, N, nb32, k;
-  QMat w0, w1;                      // gate, up (gate/up) or down (w0 only)
-  const int32_t* slot_list;
-  const int4* tiles;
-  const int32_t* n_tiles;
-  int fd, I, nb32I;                 // gate/up: down format, I, padded block count of h
-  int stage_rows;                   // rows of the LDS staging area: min(kStageRows, T)
-  FragConsts kc;
-  uint16_t *h_hi, *h_lo, *hs_hi, *hs_lo;
-  float* y;
-};
-
-template <int F>
-__device__ __forceinline__ uint4 load_d(const uint8_t* srow, int u) {
-  if constexpr (F == FMT_Q2SM) {
-    return *reinterpret_cast<const uint4*>(srow + 16 * (int64_t)u);
-  } else {
-    return make_uint4(*reinterpret_cast<const uint32_t*>(srow + 4 * (int64_t)u), 0u, 0u, 0u);
-  }
-}
-
-template <int F>
-__device__ __forceinline__ float d_of(const uint4& dw, int i) {
-  uint32_t w;
-  if constexpr (F == FMT_Q2SM) {
-    w = (i >> 1) == 0 ? dw.x : (i >> 1) == 1 ? dw.y : (i >> 1) == 2 ? dw.z : dw.w;
-  } else {
-    w = dw.x;
-  }
-  return half_bits_to_float((i & 1) ? (w >> 16) : (w & 0xFFFFu)) * kScaleD;
-}
 
 // ONE: every tile holds a single slot (one token in the batch), so only the
 // first component of each output fragment is ever needed.
@@ -300,216 +263,6 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   }
 }
 
-// ---------------------------------------------------------------------------
-// Large tiles (experts with many slots): a workgroup owns up to 128 slots of one
-// expert and 64 output columns; its 4 waves form a 2 x 2 grid, each with 64
-// slots (four 16-row fragments) by 32 columns (two 16-column tiles) per
-// matrix, over the whole contraction.  Activation fragments are read straight
-// from memory (rows past the tile read row 0; their outputs are never
-// stored), codes and scales as in the small kernel, the next unit's and the
-// next block's loads issued before the current ones are used.
-constexpr int kLargeRows = 128;
-constexpr int kLargeCols = 64;
-
-template <int F, int NM, bool LO, int MODE>
-__global__ __launch_bounds__(256) void ffn_large_kernel(FfnTileArgs a) {
-  constexpr int UB = Codes<F>::kUnitBlocks;
-  const int tile = blockIdx.y;
-  if (tile >= *a.n_tiles) return;
-  const int4 tl = a.tiles[tile];
-  const int le = tl.x, p0 = tl.y, rows = tl.z;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int r0 = 64 * wm;
-  if (r0 >= rows) return;   // this wave has no slots (the kernel has no barrier)
-  const int n_mi = min(4, (rows - r0 + 15) / 16);
-  const int n0 = blockIdx.x * kLargeCols + 32 * wn;
-  const int c16 = lane & 15, g = lane >> 4;
-  const int K = a.K, nb = K / 32;
-  const int n_units = (nb + UB - 1) / UB;
-  const int64_t rbytes = Codes<F>::row_bytes(K);
-  const int64_t sbytes = Codes<F>::scale_row_bytes(K);
-
-  const uint16_t* ah[4];
-  const uint16_t* al[4];
-  int64_t so[4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const int r = r0 + 16 * mi + c16;
-    const int rr = r < rows ? r : 0;
-    const int64_t arow = MODE == MODE_GATEUP ? a.slot_list[p0 + rr] / a.k : p0 + rr;
-    ah[mi] = a.a_hi + arow * K + 8 * g;
-    al[mi] = LO ? a.a_lo + arow * K + 8 * g : nullptr;
-    so[mi] = arow * a.nb32 + 8 * g;
-  }
-  const uint8_t* cp[kNT][NM];
-  const uint8_t* sp[kNT][NM];
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    const int64_t row = (int64_t)le * a.N + n0 + 16 * nt + c16;
-#pragma unroll
-    for (int mt = 0; mt < NM; ++mt) {
-      const QMat& w = mt ? a.w1 : a.w0;
-      cp[nt][mt] = reinterpret_cast<const uint8_t*>(w.codes) + row * rbytes + 16 * g;
-      sp[nt][mt] = reinterpret_cast<const uint8_t*>(w.scales) + row * sbytes;
-    }
-  }
-  const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-  f32x4_t acc[4][kNT][NM];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-      for (int mt = 0; mt < NM; ++mt) acc[mi][nt][mt] = zero4;
-  const uint32_t k1024v = to_vgpr(a.kc.k1024);
-
-  uint4 cw[kNT][NM], dw[kNT][NM], cwn[kNT][NM], dwn[kNT][NM];
-  auto load_unit = [&](int u, uint4 (&c)[kNT][NM], uint4 (&d)[kNT][NM]) {
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-      for (int mt = 0; mt < NM; ++mt) {
-        c[nt][mt] = *reinterpret_cast<const uint4*>(cp[nt][mt] + (int64_t)u * 64);
-        d[nt][mt] = load_d<F>(sp[nt][mt], u);
-      }
-  };
-  uint4 ahv[4], alv[4], ahn[4], aln[4];
-  auto load_a = [&](int b, uint4 (&hv)[4], uint4 (&lv)[4]) {
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      if (mi < n_mi) {
-        hv[mi] = *reinterpret_cast<const uint4*>(ah[mi] + 32 * (int64_t)b);
-        if (LO) lv[mi] = *reinterpret_cast<const uint4*>(al[mi] + 32 * (int64_t)b);
-      }
-    }
-  };
-  load_unit(0, cw, dw);
-  load_a(0, ahv, alv);
-  for (int u = 0; u < n_units; ++u) {
-    if (u + 1 < n_units) load_unit(u + 1, cwn, dwn);
-#pragma unroll
-    for (int i = 0; i < UB; ++i) {
-      const int b = u * UB + i;
-      if (b >= nb) break;
-      if (b + 1 < nb) load_a(b + 1, ahn, aln);
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-#pragma unroll
-        for (int mt = 0; mt < NM; ++mt) {
-          const uint4 bf = Codes<F>::frag(cw[nt][mt], i, a.kc, k1024v);
-          const float d = d_of<F>(dw[nt][mt], i);
-#pragma unroll
-          for (int mi = 0; mi < 4; ++mi) {
-            if (mi < n_mi) {
-              f32x4_t p = mfma16(ahv[mi], bf, zero4);
-              if (LO) p = mfma16(alv[mi], bf, p);
-#pragma unroll
-              for (int r = 0; r < 4; ++r) acc[mi][nt][mt][r] = fmaf(d, p[r], acc[mi][nt][mt][r]);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        ahv[mi] = ahn[mi];
-        if (LO) alv[mi] = aln[mi];
-      }
-    }
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-      for (int mt = 0; mt < NM; ++mt) {
-        cw[nt][mt] = cwn[nt][mt];
-        dw[nt][mt] = dwn[nt][mt];
-      }
-  }
-  if constexpr (Codes<F>::kHasM) {
-    const int n_mc = (nb + 31) / 32;
-    const int mlen = n_units * UB;
-    for (int c = 0; c < n_mc; ++c) {
-      const int b0 = 32 * c + 8 * g;
-      uint4 bm[kNT][NM];
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < NM; ++mt)
-          bm[nt][mt] = b0 < mlen ? *reinterpret_cast<const uint4*>(sp[nt][mt] + 2 * (int64_t)(mlen + b0)) : zero;
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        if (mi < n_mi) {
-          const uint4 shi = *reinterpret_cast<const uint4*>(a.s_hi + so[mi] + 32 * c);
-          const uint4 slo = *reinterpret_cast<const uint4*>(a.s_lo + so[mi] + 32 * c);
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-            for (int mt = 0; mt < NM; ++mt) {
-              acc[mi][nt][mt] = mfma16(shi, bm[nt][mt], acc[mi][nt][mt]);
-              acc[mi][nt][mt] = mfma16(slo, bm[nt][mt], acc[mi][nt][mt]);
-            }
-        }
-      }
-    }
-  }
-  // epilogue: lane holds rows r0 + 16 mi + 4g + r, columns n0 + 16 nt + c16
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    if (mi >= n_mi) break;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = r0 + 16 * mi + 4 * g + r;
-      const bool valid = row < rows;
-      if constexpr (MODE == MODE_DOWN) {
-        if (valid) {
-          const int64_t slot = a.slot_list[p0 + row];
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt)
-            a.y[slot * a.N + n0 + 16 * nt + c16] = acc[mi][nt][0][r] * (1.0f / kSigmaH);
-        }
-      } else {
-        float hsum = 0.0f;
-        if (valid) {
-          const float inv = 1.0f / a.sigma[a.slot_list[p0 + row] / a.k];   // a power of two: exact
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) {
-            const float h = silu(acc[mi][nt][0][r] * inv) * (acc[mi][nt][1][r] * inv);
-            const int col = n0 + 16 * nt + c16;
-            const int blk = col >> 5, kk = col & 31, gg = kk >> 3;
-            const int e = elem_of_rt(a.fd, kk & 7);
-            uint32_t hi, lo;
-            split_f16(h * ldexpf(1.0f, -pos_rt(a.fd, e)), hi, lo);
-            const int64_t at = (int64_t)(p0 + row) * a.I + 32 * blk + 8 * gg + e;
-            a.h_hi[at] = (uint16_t)hi;
-            a.h_lo[at] = (uint16_t)lo;
-            hsum += h;
-          }
-        }
-        // block sum over the wave's 32 columns of this row: 16 lanes, fixed order
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) hsum += __shfl_xor(hsum, m, kWave);
-        if (valid && c16 == 0) {
-          uint32_t hi, lo;
-          split_f16(hsum * kSigmaH, hi, lo);
-          const int64_t at = (int64_t)(p0 + row) * a.nb32I + n0 / 32;
-          a.hs_hi[at] = (uint16_t)hi;
-          a.hs_lo[at] = (uint16_t)lo;
-        }
-      }
-    }
-  }
-  if (MODE == MODE_GATEUP && blockIdx.x == 0 && wn == 0) {
-    const int nbI = a.I / 32, npad = a.nb32I - nbI;
-    for (int j = lane; j < 64 * npad; j += kWave) {
-      const int row = r0 + j % 64, bb = nbI + j / 64;
-      if (row < rows) {
-        a.hs_hi[(int64_t)(p0 + row) * a.nb32I + bb] = 0;
-        a.hs_lo[(int64_t)(p0 + row) * a.nb32I + bb] = 0;
-      }
-    }
-  }
-}
-
 template <int F, int NM, bool LO, int MODE, bool ONE>
 static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_t s) {
   const size_t stage = (size_t)t.stage_rows * t.K * 2 * (LO ? 2 : 1) + (size_t)t.K * 2;
@@ -522,12 +275,6 @@ static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_
     if (e != hipSuccess) return e;
   }
   kern<<<dim3(t.N / (16 * kNT), max_tiles), kFfnThreads, lds, s>>>(t);
-  return hipGetLastError();
-}
-
-template <int F, int NM, bool LO, int MODE>
-static hipError_t launch_large_t(const FfnTileArgs& t, int max_tiles, hipStream_t s) {
-  ffn_large_kernel<F, NM, LO, MODE><<<dim3(t.N / kLargeCols, max_tiles), 256, 0, s>>>(t);
   return hipGetLastError();
 }
 
@@ -547,7 +294,6 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   const bool one = a.T == 1;
 #define MOE_SMALL(F, NM, LO, MODE) \
   (one ? launch_small_t<F, NM, LO, MODE, true>(t, a.max_small, s) : launch_small_t<F, NM, LO, MODE, false>(t, a.max_small, s))
-#define MOE_LARGE(F, NM, LO, MODE) launch_large_t<F, NM, LO, MODE>(t, a.max_large, s)
   t.tiles = a.small; t.n_tiles = a.n_small;
   trace_pre("ffn_gateup", s);
   if (a.fg == FMT_Q2SM)
@@ -559,10 +305,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.max_large > 0) {
     t.tiles = a.large; t.n_tiles = a.n_large;
     trace_pre("ffn_gateup_large", s);
-    if (a.fg == FMT_Q2SM)
-      err = lo ? MOE_LARGE(FMT_Q2SM, 2, true, MODE_GATEUP) : MOE_LARGE(FMT_Q2SM, 2, false, MODE_GATEUP);
-    else
-      err = lo ? MOE_LARGE(FMT_Q8_0, 2, true, MODE_GATEUP) : MOE_LARGE(FMT_Q8_0, 2, false, MODE_GATEUP);
+    err = launch_large(t, a.fg, MODE_GATEUP, lo, a.max_large, s);
     trace_post("ffn_gateup_large", s);
     if (err != hipSuccess) return err;
   }
@@ -578,11 +321,10 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.max_large > 0) {
     t.tiles = a.large; t.n_tiles = a.n_large;
     trace_pre("ffn_down_large", s);
-    err = a.fd == FMT_Q2SM ? MOE_LARGE(FMT_Q2SM, 1, true, MODE_DOWN) : MOE_LARGE(FMT_Q8_0, 1, true, MODE_DOWN);
+    err = launch_large(t, a.fd, MODE_DOWN, true, a.max_large, s);
     trace_post("ffn_down_large", s);
   }
 #undef MOE_SMALL
-#undef MOE_LARGE
   return err;
 }
 
