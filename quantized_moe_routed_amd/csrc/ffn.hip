@@ -57,19 +57,25 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   const int64_t rbytes = Codes<F>::row_bytes(K);
   const int64_t sbytes = Codes<F>::scale_row_bytes(K);
 
-  // weight rows of this workgroup's output columns
-  const uint8_t* cp[kNT][NM];
-  const uint8_t* sp[kNT][NM];
+  // weight rows of this workgroup's output columns: the expert's matrices (uniform bases) and the
+  // lane's byte offsets within them (one matrix is well under 4 GiB)
+  const uint8_t* cb[NM];
+  const uint8_t* sb[NM];
+#pragma unroll
+  for (int mt = 0; mt < NM; ++mt) {
+    const QMat& w = mt ? a.w1 : a.w0;
+    cb[mt] = reinterpret_cast<const uint8_t*>(w.codes) + (int64_t)le * a.N * rbytes;
+    sb[mt] = reinterpret_cast<const uint8_t*>(w.scales) + (int64_t)le * a.N * sbytes;
+  }
+  uint32_t co[kNT], so[kNT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
-    const int64_t row = (int64_t)le * a.N + n0 + 16 * nt + c16;
-#pragma unroll
-    for (int mt = 0; mt < NM; ++mt) {
-      const QMat& w = mt ? a.w1 : a.w0;
-      cp[nt][mt] = reinterpret_cast<const uint8_t*>(w.codes) + row * rbytes + 16 * g;
-      sp[nt][mt] = reinterpret_cast<const uint8_t*>(w.scales) + row * sbytes;
-    }
+    const uint32_t col = (uint32_t)(n0 + 16 * nt + c16);
+    co[nt] = col * (uint32_t)rbytes + 16u * (uint32_t)g;
+    so[nt] = col * (uint32_t)sbytes;
   }
+  auto cp = [&](int nt, int mt, int u) { return cb[mt] + (co[nt] + 64u * (uint32_t)u); };
+  auto sp = [&](int nt, int mt) { return sb[mt] + so[nt]; };
   const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
   const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
   // this wave's code units: a contiguous range (contiguous bytes of every row it reads)
@@ -84,8 +90,8 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
       for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt) {
-          cw[j][nt][mt] = *reinterpret_cast<const uint4*>(cp[nt][mt] + (int64_t)u * 64);
-          dw[j][nt][mt] = load_d<F>(sp[nt][mt], u);
+          cw[j][nt][mt] = *reinterpret_cast<const uint4*>(cp(nt, mt, u));
+          dw[j][nt][mt] = load_d<F>(sp(nt, mt), u);
         }
     }
   };
@@ -124,7 +130,21 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   const uint16_t* pa = (mvalid ? (c16 < 4 ? st_hi : st_lo) + slot_m * K : st_zero) + 8 * g;
   // the m-term operand: rows 0..3 hi, 4..7 lo of the block sums
   const bool svalid = slot_m < rows && c16 < 8;
-  const uint16_t* ps = (c16 < 4 ? a.s_hi : a.s_lo) + (int64_t)arow * a.nb32 + 8 * g;
+  const uint16_t* ps = (c16 < 4 ? a.s_hi : a.s_lo) + (int64_t)arow * a.nb32;
+  // m-term operands of a group of up to 4 of this wave's units (lane group g: unit ug + g): the m
+  // values of the lane's column and the block sums of the slots (rows 0..3 hi, 4..7 lo)
+  const int mlen = n_units * UB;   // entries of the m row
+  uint4 mv[kNT][NM], sv = zero;
+  auto load_mterm = [&](int ug) {
+    const int u = ug + g;
+    const bool in = u < u_end;
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt)
+        mv[nt][mt] = in ? *reinterpret_cast<const uint4*>(sp(nt, mt) + 2u * (uint32_t)(mlen + UB * u)) : zero;
+    sv = in && svalid ? *reinterpret_cast<const uint4*>(ps + UB * u) : zero;
+  };
 
   f32x4_t acc[kNT][NM];
 #pragma unroll
@@ -166,20 +186,15 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
       }
     }
   }
-  // m-term over the block index, 32 blocks per product (2-bit blocks only)
+  // m-term over the block index (2-bit blocks only): each wave adds sum_b m_b (sigma S_b) over its
+  // own units, four units (32 blocks) per product
   if constexpr (Codes<F>::kHasM) {
-    const int n_mc = (nb + 31) / 32;
-    const int mlen = n_units * UB;   // entries of the m row
-    for (int c = wave; c < n_mc; c += kFfnWaves) {
-      const uint4 sv = svalid ? *reinterpret_cast<const uint4*>(ps + 32 * c) : zero;
-      const int b0 = 32 * c + 8 * g;
+    for (int ug = u_beg; ug < u_end; ug += 4) {
+      load_mterm(ug);
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < NM; ++mt) {
-          const uint4 bm = b0 < mlen ? *reinterpret_cast<const uint4*>(sp[nt][mt] + 2 * (int64_t)(mlen + b0)) : zero;
-          acc[nt][mt] = mfma16(sv, bm, acc[nt][mt]);   // same units as the d-term: sigma * value
-        }
+        for (int mt = 0; mt < NM; ++mt) acc[nt][mt] = mfma16(sv, mv[nt][mt], acc[nt][mt]);   // sigma * value units
     }
   }
   // partial sums of the four waves, added in wave order (the staging area is reused)

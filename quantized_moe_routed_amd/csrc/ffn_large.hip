@@ -14,8 +14,10 @@
 //     They are fetched by direct global->LDS loads, in stages of 8 blocks
 //     (4 when the operand has a lo plane), double-buffered: the loads of stage
 //     s+1 are in flight while stage s is multiplied.  Within a 64-byte row
-//     block the four 16-byte groups are stored XOR-swizzled by row, so the
-//     fragment reads of 8 consecutive lanes hit 8 distinct bank groups.
+//     block the four 16-byte groups are stored XOR-swizzled by (row / 4) mod 4,
+//     so the 16-byte fragment reads of 16 consecutive lanes (16 rows) cover 16
+//     distinct 16-byte bank groups: no bank conflicts (measured with the LDS
+//     bank-conflict counter).
 //   * Each wave reads the codes and scales of its own columns straight into
 //     registers, one load group ahead (a 2-bit unit of 8 blocks, or a Q8_0 unit
 //     of 2 blocks).
@@ -157,7 +159,7 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
   // group (lane & 3) ^ swizzle of its LDS slot
   constexpr int GPW = C::GPW;
   const int rl = lane >> 2;
-  const int grp = (lane & 3) ^ ((rl >> 1) & 3);
+  const int grp = (lane & 3) ^ ((rl >> 2) & 3);
   const uint8_t* arow[GPW];
 #pragma unroll
   for (int j = 0; j < GPW; ++j) {
@@ -191,7 +193,7 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
   // fragment reads: row 32 mi + c32, 16-byte group 2 h + g2 at its swizzled slot
   uint32_t aoff[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) aoff[h] = (uint32_t)(c32 * 64 + (((2 * h + g2) ^ ((c32 >> 1) & 3)) * 16));
+  for (int h = 0; h < 2; ++h) aoff[h] = (uint32_t)(c32 * 64 + (((2 * h + g2) ^ ((c32 >> 2) & 3)) * 16));
 
   f32x16_t acc[MI > 0 ? MI : 1][NT2][NM];
 #pragma unroll
