@@ -78,20 +78,23 @@ typedef enum { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 } moe_act;
 
 /* A stack of n matrices, each `rows` outputs x `cols` inputs, in the planar
  * device layout written by moe_pack_planar() (sizes from moe_planar_bytes()).
- * nb = cols/32 blocks per row.  Codes are cut into 64-byte units per row so
+ * nb = cols/32 blocks per row.  A row's codes are cut into 64-byte units so
  * that the lane that owns values 8g..8g+7 of a block (g = 0..3, the K-group of
  * a 16x16x32 matrix-core fragment) reads exactly its codes with one 16-byte
  * load:
+ *   Q8_0 : units of 2 blocks; in unit j the 16 bytes at 16g are
+ *          {block 2j q[8g..8g+7], block 2j+1 q[8g..8g+7]}.
+ *   Q2SM : units of 8 blocks; in unit j the 16 bytes at 16g are 4 words,
+ *          word i = {block 8j+2i byte 2g, block 8j+2i+1 byte 2g, block 8j+2i
+ *          byte 2g+1, block 8j+2i+1 byte 2g+1}, where byte r of a block holds
+ *          its values 4r..4r+3 (2 bits each, value 4r+s at bits 2s..2s+1).
+ * Rows are taken in groups of 16 (the last group padded with zero rows); with
+ * U = units per row, each matrix is
+ *   codes  = [ceil(rows/16)][U][16 rows][64 bytes]: one unit of 16 rows is
+ *            1 KiB of consecutive bytes;
+ *   scales = Q8_0: [ceil(rows/16)][U][16 rows][2 fp16 d];
+ *            Q2SM: [ceil(rows/16)][U] { [16 rows][8 fp16 d], [16 rows][8 fp16 m] }.
  *   F32  : codes = float [n][rows][cols];  scales = NULL.
- *   Q8_0 : codes = [n][rows][ceil(nb/2)] units of 2 blocks; in unit j the 16
- *          bytes at 16g are {block 2j q[8g..8g+7], block 2j+1 q[8g..8g+7]};
- *          scales = fp16 d [n][rows][2*ceil(nb/2)].
- *   Q2SM : codes = [n][rows][ceil(nb/8)] units of 8 blocks; in unit j the 16
- *          bytes at 16g are 4 words, word i = {block 8j+2i byte 2g, block
- *          8j+2i+1 byte 2g, block 8j+2i byte 2g+1, block 8j+2i+1 byte 2g+1},
- *          where byte r of a block holds its values 4r..4r+3 (2 bits each,
- *          value 4r+s at bits 2s..2s+1);
- *          scales = per row, 8*ceil(nb/8) fp16 d values, then as many fp16 m.
  * Blocks past nb (padding of a row's last unit) have zero codes and scales.
  * cols must be a multiple of 32. */
 typedef struct {

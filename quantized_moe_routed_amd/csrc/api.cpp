@@ -411,14 +411,16 @@ moe_status moe_combine(const float* y_slot, const float* w, const int32_t* ids, 
 
 // ---- host helpers ---------------------------------------------------------------
 
+static size_t groups16(int64_t rows) { return (size_t)((rows + 15) / 16); }
+
 moe_status moe_planar_bytes(int32_t fmt, int32_t rows, int32_t cols, size_t* codes_bytes, size_t* scales_bytes) {
   if (rows < 0 || cols <= 0 || cols % 32) return fail(MOE_ERR_ARG, "moe_planar_bytes: bad shape %dx%d", rows, cols);
   size_t c, sc;
   const size_t nb = (size_t)(cols / 32);
   switch (fmt) {
     case MOE_W_F32: c = (size_t)rows * cols * 4; sc = 0; break;
-    case MOE_W_Q8_0: c = (size_t)rows * ((nb + 1) / 2) * 64; sc = (size_t)rows * ((nb + 1) / 2) * 4; break;
-    case MOE_W_Q2SM: c = (size_t)rows * ((nb + 7) / 8) * 64; sc = (size_t)rows * ((nb + 7) / 8) * 32; break;
+    case MOE_W_Q8_0: c = groups16(rows) * ((nb + 1) / 2) * 1024; sc = groups16(rows) * ((nb + 1) / 2) * 64; break;
+    case MOE_W_Q2SM: c = groups16(rows) * ((nb + 7) / 8) * 1024; sc = groups16(rows) * ((nb + 7) / 8) * 512; break;
     default: return fail(MOE_ERR_UNSUPPORTED, "moe_planar_bytes: unknown format %d", fmt);
   }
   if (codes_bytes) *codes_bytes = c;
@@ -441,31 +443,46 @@ moe_status moe_pack_planar(int32_t fmt, int32_t n, int32_t rows, int32_t cols, c
       std::memcpy(dc, src, (size_t)nrows * cols * 4);
       break;
     case MOE_W_Q8_0: {
-      const int64_t rb = (nb + 1) / 2 * 64, sb = (nb + 1) / 2 * 4;
-      std::memset(dc, 0, (size_t)(nrows * rb));
-      std::memset(ds, 0, (size_t)(nrows * sb));
+      // row groups of 16 rows; per (group, unit of 2 blocks): 16 rows x 64 code bytes, and
+      // 16 rows x 2 fp16 d
+      const int64_t nu = (nb + 1) / 2, rg = (int64_t)groups16(rows);
+      const int64_t mc = rg * nu * 1024, ms = rg * nu * 64;   // bytes per matrix
+      std::memset(dc, 0, (size_t)(n * mc));
+      std::memset(ds, 0, (size_t)(n * ms));
       for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t mat = r / rows, row = r % rows;
+        uint8_t* mcodes = dc + mat * mc;
+        uint8_t* mscales = ds + mat * ms;
         for (int64_t b = 0; b < nb; ++b) {
           const uint8_t* blk = src + (r * nb + b) * 34;
-          std::memcpy(ds + r * sb + 2 * b, blk, 2);
+          const int64_t u = b / 2, h = b % 2;
+          std::memcpy(mscales + ((row / 16) * nu + u) * 64 + (row % 16) * 4 + 2 * h, blk, 2);
           for (int g = 0; g < 4; ++g)
-            std::memcpy(dc + r * rb + (b / 2) * 64 + g * 16 + (b % 2) * 8, blk + 2 + 8 * g, 8);
+            std::memcpy(mcodes + ((row / 16) * nu + u) * 1024 + (row % 16) * 64 + g * 16 + h * 8, blk + 2 + 8 * g, 8);
         }
       }
       break;
     }
     case MOE_W_Q2SM: {
-      const int64_t rb = (nb + 7) / 8 * 64, nbp = (nb + 7) / 8 * 8;
-      std::memset(dc, 0, (size_t)(nrows * rb));
-      std::memset(ds, 0, (size_t)(nrows * nbp * 4));
+      // row groups of 16 rows; per (group, unit of 8 blocks): 16 rows x 64 code bytes, and
+      // 16 rows x 8 fp16 d followed by 16 rows x 8 fp16 m
+      const int64_t nu = (nb + 7) / 8, rg = (int64_t)groups16(rows);
+      const int64_t mc = rg * nu * 1024, ms = rg * nu * 512;
+      std::memset(dc, 0, (size_t)(n * mc));
+      std::memset(ds, 0, (size_t)(n * ms));
       for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t mat = r / rows, row = r % rows;
+        uint8_t* mcodes = dc + mat * mc;
+        uint8_t* mscales = ds + mat * ms;
         for (int64_t b = 0; b < nb; ++b) {
           const uint8_t* blk = src + (r * nb + b) * 12;
-          std::memcpy(ds + r * nbp * 4 + 2 * b, blk, 2);              // d row
-          std::memcpy(ds + r * nbp * 4 + 2 * (nbp + b), blk + 2, 2);  // m row
-          const int64_t i = (b % 8) / 2, h = b % 2;
+          const int64_t u = b / 8, k = b % 8;
+          uint8_t* su = mscales + ((row / 16) * nu + u) * 512;
+          std::memcpy(su + (row % 16) * 16 + 2 * k, blk, 2);         // d
+          std::memcpy(su + 256 + (row % 16) * 16 + 2 * k, blk + 2, 2);  // m
+          const int64_t i = k / 2, h = k % 2;
           for (int g = 0; g < 4; ++g) {
-            uint8_t* w = dc + r * rb + (b / 8) * 64 + g * 16 + i * 4;
+            uint8_t* w = mcodes + ((row / 16) * nu + u) * 1024 + (row % 16) * 64 + g * 16 + i * 4;
             w[h] = blk[4 + 2 * g];
             w[2 + h] = blk[4 + 2 * g + 1];
           }

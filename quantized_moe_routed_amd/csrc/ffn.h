@@ -24,12 +24,13 @@ struct FfnTileArgs {
   float* y;
 };
 
+// The d values of one row in one unit (at p): 8 fp16 (Q2SM) or 2 fp16 (Q8_0, in .x).
 template <int F>
-__device__ __forceinline__ uint4 load_d(const uint8_t* srow, int u) {
+__device__ __forceinline__ uint4 load_d(const uint8_t* p) {
   if constexpr (F == FMT_Q2SM) {
-    return *reinterpret_cast<const uint4*>(srow + 16 * (int64_t)u);
+    return *reinterpret_cast<const uint4*>(p);
   } else {
-    return make_uint4(*reinterpret_cast<const uint32_t*>(srow + 4 * (int64_t)u), 0u, 0u, 0u);
+    return make_uint4(*reinterpret_cast<const uint32_t*>(p), 0u, 0u, 0u);
   }
 }
 

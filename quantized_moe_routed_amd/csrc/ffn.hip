@@ -67,15 +67,17 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
     cb[mt] = reinterpret_cast<const uint8_t*>(w.codes) + (int64_t)le * a.N * rbytes;
     sb[mt] = reinterpret_cast<const uint8_t*>(w.scales) + (int64_t)le * a.N * sbytes;
   }
+  // (row-group layout: a 16-column tile is one row group, unit u of it 1 KiB at 1 KiB * u)
   uint32_t co[kNT], so[kNT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
-    const uint32_t col = (uint32_t)(n0 + 16 * nt + c16);
-    co[nt] = col * (uint32_t)rbytes + 16u * (uint32_t)g;
-    so[nt] = col * (uint32_t)sbytes;
+    const int col = n0 + 16 * nt + c16;
+    co[nt] = (uint32_t)code_off(col, 0, n_units) + 16u * (uint32_t)g;
+    so[nt] = (uint32_t)Codes<F>::d_off(col, 0, n_units);
   }
-  auto cp = [&](int nt, int mt, int u) { return cb[mt] + (co[nt] + 64u * (uint32_t)u); };
-  auto sp = [&](int nt, int mt) { return sb[mt] + so[nt]; };
+  // codes of unit u; d values of unit u (m values of a 2-bit unit follow its d values of 16 rows)
+  auto cp = [&](int nt, int mt, int u) { return cb[mt] + (co[nt] + 1024u * (uint32_t)u); };
+  auto dp = [&](int nt, int mt, int u) { return sb[mt] + (so[nt] + (uint32_t)Codes<F>::kScaleUnit * (uint32_t)u); };
   const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
   const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
   // this wave's code units: a contiguous range (contiguous bytes of every row it reads)
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt) {
           cw[j][nt][mt] = *reinterpret_cast<const uint4*>(cp(nt, mt, u));
-          dw[j][nt][mt] = load_d<F>(sp(nt, mt), u);
+          dw[j][nt][mt] = load_d<F>(dp(nt, mt, u));
         }
     }
   };
@@ -133,7 +135,6 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   const uint16_t* ps = (c16 < 4 ? a.s_hi : a.s_lo) + (int64_t)arow * a.nb32;
   // m-term operands of a group of up to 4 of this wave's units (lane group g: unit ug + g): the m
   // values of the lane's column and the block sums of the slots (rows 0..3 hi, 4..7 lo)
-  const int mlen = n_units * UB;   // entries of the m row
   uint4 mv[kNT][NM], sv = zero;
   auto load_mterm = [&](int ug) {
     const int u = ug + g;
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
     for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
       for (int mt = 0; mt < NM; ++mt)
-        mv[nt][mt] = in ? *reinterpret_cast<const uint4*>(sp(nt, mt) + 2u * (uint32_t)(mlen + UB * u)) : zero;
+        mv[nt][mt] = in ? *reinterpret_cast<const uint4*>(dp(nt, mt, u) + 256u) : zero;
     sv = in && svalid ? *reinterpret_cast<const uint4*>(ps + UB * u) : zero;
   };
 

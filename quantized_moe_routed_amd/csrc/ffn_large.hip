@@ -97,20 +97,27 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
   const int64_t rbytes = Codes<F>::row_bytes(K);
   const int64_t sbytes = Codes<F>::scale_row_bytes(K);
 
+  // the expert's matrices (uniform bases) and the lane's offsets in the row-group layout: column
+  // n0 + 32 nt + c32 is row c32 % 16 of a group; unit u adds 1 KiB (codes) or the scale unit
   bool colv[NT2];
-  const uint8_t* cp[NT2][NM];
-  const uint8_t* sp[NT2][NM];
+  const uint8_t* cb[NM];
+  const uint8_t* sb[NM];
+#pragma unroll
+  for (int mt = 0; mt < NM; ++mt) {
+    const QMat& w = mt ? a.w1 : a.w0;
+    cb[mt] = reinterpret_cast<const uint8_t*>(w.codes) + (int64_t)le * N * rbytes;
+    sb[mt] = reinterpret_cast<const uint8_t*>(w.scales) + (int64_t)le * N * sbytes;
+  }
+  uint32_t co[NT2], so[NT2];
 #pragma unroll
   for (int nt = 0; nt < NT2; ++nt) {
     colv[nt] = n0 + 32 * nt < N;
-    const int64_t row = (int64_t)le * N + (colv[nt] ? n0 + 32 * nt : N - 32) + c32;
-#pragma unroll
-    for (int mt = 0; mt < NM; ++mt) {
-      const QMat& w = mt ? a.w1 : a.w0;
-      cp[nt][mt] = reinterpret_cast<const uint8_t*>(w.codes) + row * rbytes + 16 * g2;
-      sp[nt][mt] = reinterpret_cast<const uint8_t*>(w.scales) + row * sbytes;
-    }
+    const int col = (colv[nt] ? n0 + 32 * nt : N - 32) + c32;
+    co[nt] = (uint32_t)code_off(col, 0, n_units) + 16u * (uint32_t)g2;
+    so[nt] = (uint32_t)Codes<F>::d_off(col, 0, n_units);
   }
+  auto cp = [&](int nt, int mt, int u) { return cb[mt] + (co[nt] + 1024u * (uint32_t)u); };
+  auto dp = [&](int nt, int mt, int u) { return sb[mt] + (so[nt] + (uint32_t)Codes<F>::kScaleUnit * (uint32_t)u); };
   // Weight registers.  A load group is what one stage consumes: one 2-bit unit (8 blocks, also
   // when a stage holds 4), or SB / 2 Q8_0 units.  For each unit: the codes of 16-byte groups g2
   // and g2 + 2 of the lane's column, and the unit's scales.
@@ -129,10 +136,10 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
       for (int nt = 0; nt < NT2; ++nt)
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt) {
-          const uint8_t* c = cp[nt][mt] + (int64_t)uc * 64;
+          const uint8_t* c = cp(nt, mt, uc);
           cwn[j][nt][mt][0] = *reinterpret_cast<const uint4*>(c);
           cwn[j][nt][mt][1] = *reinterpret_cast<const uint4*>(c + 32);
-          dwn[j][nt][mt] = load_d<F>(sp[nt][mt], uc);
+          dwn[j][nt][mt] = load_d<F>(dp(nt, mt, uc));
         }
     }
   };
@@ -334,7 +341,7 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
 
   if constexpr (Codes<F>::kHasM && MI > 0) {
     // sum_b m_b (sigma S_b): block index as the contraction, 32 blocks per step
-    const int mlen = n_units * UB;
+    const int mlen = n_units * UB;   // blocks covered by the units (the rest of a step is zero)
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
     for (int c = 0; c < (nb + 31) / 32; ++c) {
       uint4 bm[NT2][NM][2];
@@ -345,7 +352,7 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int bb = 32 * c + 16 * h + 8 * g2;
-            bm[nt][mt][h] = bb < mlen ? *reinterpret_cast<const uint4*>(sp[nt][mt] + 2 * (int64_t)(mlen + bb)) : zero;
+            bm[nt][mt][h] = bb < mlen ? *reinterpret_cast<const uint4*>(dp(nt, mt, bb / UB) + 256u) : zero;
           }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {

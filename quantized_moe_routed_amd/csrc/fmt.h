@@ -20,18 +20,20 @@
 // the second sum (S_b = block sum of a; Q2SM only, Q8_0 has m = 0) being one
 // more small matrix product over the block index.
 
-// Planar code layouts (bytes of the definition blocks, re-laid so that the
-// lane with K-group g of a 16x16x32 fragment reads exactly its own codes with
-// one 16-byte load; g covers values 8g..8g+7 of each block):
-//   Q2SM: a row is a sequence of 64-byte units of 8 blocks; in unit j the 16
-//         bytes of group g are 4 words, word i = [blk 2i byte 2g, blk 2i+1
-//         byte 2g, blk 2i byte 2g+1, blk 2i+1 byte 2g+1] (blk = block 8j+..).
-//   Q8_0: a row is a sequence of 64-byte units of 2 blocks; in unit j the 16
-//         bytes of group g are [blk 2j q[8g..8g+7], blk 2j+1 q[8g..8g+7]].
-//   Missing blocks of a row's last unit are zero.
-// Planar scale layouts (one row per matrix row, padded to whole units, padding
-// zero): Q2SM: the unit-padded fp16 d values of the row, then its fp16 m
-// values; Q8_0: the unit-padded fp16 d values.
+// Planar layouts.  A row's codes are cut into 64-byte units (8 blocks of
+// Q2SM, 2 blocks of Q8_0) in which the lane with K-group g of a 16x16x32
+// fragment (values 8g..8g+7 of each block) finds its codes in the 16 bytes at
+// 16g:
+//   Q2SM: word i of those 16 bytes = [blk 2i byte 2g, blk 2i+1 byte 2g,
+//         blk 2i byte 2g+1, blk 2i+1 byte 2g+1] (blk = block 8j+.. of unit j).
+//   Q8_0: the 16 bytes are [blk 2j q[8g..8g+7], blk 2j+1 q[8g..8g+7]].
+// Rows are taken in groups of 16, and a group stores unit by unit the 16
+// rows' 64-byte units one after the other: a wave's load of one unit of 16
+// rows reads 1 KiB of consecutive bytes.  Scales follow the same grouping:
+// per (row group, unit), Q2SM the 16 rows' 8 fp16 d values (256 bytes) then
+// their 8 fp16 m values (256 bytes); Q8_0 the 16 rows' 2 fp16 d values
+// (64 bytes).  Missing blocks of a row's last unit, and the rows that pad the
+// last group to 16, are zero.
 #pragma once
 #include "device.h"
 
@@ -96,10 +98,22 @@ inline FragConsts frag_consts() {
                     0x64646464u, 0xE480E480u, 0x04020400u, 0x04030401u};
 }
 
+// Byte offsets in the row-group layout (n_units units per row).
+__host__ __device__ constexpr int64_t code_off(int row, int unit, int n_units) {
+  return ((int64_t)(row >> 4) * n_units + unit) * 1024 + (row & 15) * 64;
+}
+
 template <>
 struct Codes<FMT_Q2SM> {
   static constexpr int kUnitBlocks = 8;
   static constexpr bool kHasM = true;
+  static constexpr int kDBytes = 16;      // d bytes of one row in one unit (8 fp16)
+  static constexpr int kScaleUnit = 512;  // scale bytes of a (row group, unit): 16 rows of d, then of m
+  static constexpr int kMOffset = 256;    // m values of a (row group, unit) after its d values
+  __host__ __device__ static constexpr int64_t d_off(int row, int unit, int n_units) {
+    return ((int64_t)(row >> 4) * n_units + unit) * kScaleUnit + (row & 15) * kDBytes;
+  }
+  // code and scale bytes per row (a matrix of 16 r rows takes r times 16 of these)
   __host__ __device__ static constexpr int64_t row_bytes(int cols) { return (int64_t)((cols / 32 + 7) / 8) * 64; }
   __host__ __device__ static constexpr int64_t scale_row_bytes(int cols) { return (int64_t)((cols / 32 + 7) / 8) * 32; }
   // B fragment of block i (0..7) of a unit from the lane's 16-byte chunk
@@ -120,6 +134,11 @@ template <>
 struct Codes<FMT_Q8_0> {
   static constexpr int kUnitBlocks = 2;
   static constexpr bool kHasM = false;
+  static constexpr int kDBytes = 4;       // d bytes of one row in one unit (2 fp16)
+  static constexpr int kScaleUnit = 64;   // scale bytes of a (row group, unit)
+  __host__ __device__ static constexpr int64_t d_off(int row, int unit, int n_units) {
+    return ((int64_t)(row >> 4) * n_units + unit) * kScaleUnit + (row & 15) * kDBytes;
+  }
   __host__ __device__ static constexpr int64_t row_bytes(int cols) { return (int64_t)((cols / 32 + 1) / 2) * 64; }
   __host__ __device__ static constexpr int64_t scale_row_bytes(int cols) { return (int64_t)((cols / 32 + 1) / 2) * 4; }
   __device__ static __forceinline__ uint4 frag(const uint4& c, int i, const FragConsts& k, uint32_t) {

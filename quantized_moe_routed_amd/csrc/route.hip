@@ -14,6 +14,7 @@
 // Lanes past the last block contribute +0.0: padding the tree with zeros
 // changes no value, so the result equals the carry-up tree for any block count.
 #include "device.h"
+#include "fmt.h"
 #include "launch.h"
 
 namespace moe {
@@ -39,9 +40,9 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
     dsc[j] = 0.0f;
     if (b < nb) {
       if constexpr (FMT == FMT_Q8_0) {
-        // unit layout: block b's values 8g..8g+7 at unit b/2, group g, half b%2
-        const int8_t* q = reinterpret_cast<const int8_t*>(codes) + (int64_t)e * ((nb + 1) / 2) * 64 +
-                          (b >> 1) * 64 + (b & 1) * 8;
+        // row-group layout: block b's values 8g..8g+7 in unit b/2 of row e, group g, half b%2
+        const int nu = (nb + 1) / 2;
+        const int8_t* q = reinterpret_cast<const int8_t*>(codes) + code_off(e, b >> 1, nu) + (b & 1) * 8;
         int words[8];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -51,7 +52,8 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
         }
 #pragma unroll
         for (int i = 0; i < 32; ++i) wv[j][i] = (float)(int8_t)(words[i / 4] >> (8 * (i % 4)));
-        dsc[j] = half_bits_to_float(reinterpret_cast<const uint16_t*>(scales)[(int64_t)e * ((nb + 1) / 2 * 2) + b]);
+        dsc[j] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(
+            reinterpret_cast<const uint8_t*>(scales) + Codes<FMT_Q8_0>::d_off(e, b >> 1, nu) + 2 * (b & 1)));
       } else {
         const float4* w4 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(codes) +
                                                            (int64_t)e * H + b * 32);

@@ -32,39 +32,43 @@ def test_version():
 
 
 def decode_planar(fmt, codes, scales, n, rows, cols):
-    """Values of n planar matrices, decoded from the unit layout as include/moe.h documents it."""
+    """Values of n planar matrices, decoded from the row-group layout as include/moe.h documents it."""
     nb = cols // 32
-    out = np.zeros((n * rows, cols))
     if fmt == 0:
         return codes.view(np.float32).astype(np.float64).reshape(n * rows, cols)
+    rg = (rows + 15) // 16
+    out = np.zeros((n, rg * 16, cols))
     if fmt == 1:
-        rb = (nb + 1) // 2 * 64
-        c = codes.reshape(n * rows, rb)
-        d = scales.view(np.float16).astype(np.float64).reshape(n * rows, (nb + 1) // 2 * 2)
+        nu = (nb + 1) // 2
+        c = codes.reshape(n, rg, nu, 16, 64)
+        d = scales.view(np.float16).astype(np.float64).reshape(n, rg, nu, 16, 2)
         for b in range(nb):
+            u, h = b // 2, b % 2
             for g in range(4):
-                o = (b // 2) * 64 + g * 16 + (b % 2) * 8
-                q = c[:, o:o + 8].view(np.int8).astype(np.float64)
-                out[:, 32 * b + 8 * g:32 * b + 8 * g + 8] = d[:, b:b + 1] * q
-        return out
-    rb = (nb + 7) // 8 * 64
-    nbp = (nb + 7) // 8 * 8
-    c = codes.reshape(n * rows, rb)
-    sc = scales.view(np.float16).astype(np.float64).reshape(n * rows, 2, nbp)   # d row, then m row
-    dm = np.stack([sc[:, 0, :nb], sc[:, 1, :nb]], -1)
-    for b in range(nb):
-        i, h = (b % 8) // 2, b % 2
-        for g in range(4):
-            w = (b // 8) * 64 + g * 16 + i * 4
-            lo_byte, hi_byte = c[:, w + h], c[:, w + 2 + h]        # definition bytes 2g and 2g+1
-            for s in range(4):
-                out[:, 32 * b + 8 * g + s] = dm[:, b, 0] * ((lo_byte >> (2 * s)) & 3) + dm[:, b, 1]
-                out[:, 32 * b + 8 * g + 4 + s] = dm[:, b, 0] * ((hi_byte >> (2 * s)) & 3) + dm[:, b, 1]
-    return out
+                q = c[:, :, u, :, 16 * g + 8 * h:16 * g + 8 * h + 8].view(np.int8).astype(np.float64)
+                out[:, :, 32 * b + 8 * g:32 * b + 8 * g + 8] = (d[:, :, u, :, h:h + 1] * q).reshape(n, rg * 16, 8)
+    else:
+        nu = (nb + 7) // 8
+        c = codes.reshape(n, rg, nu, 16, 64)
+        sc = scales.view(np.float16).astype(np.float64).reshape(n, rg, nu, 2, 16, 8)   # d rows, then m rows
+        for b in range(nb):
+            u, k = b // 8, b % 8
+            i, h = k // 2, k % 2
+            d = sc[:, :, u, 0, :, k].reshape(n, rg * 16)
+            m = sc[:, :, u, 1, :, k].reshape(n, rg * 16)
+            for g in range(4):
+                lo_byte = c[:, :, u, :, 16 * g + 4 * i + h].reshape(n, rg * 16)       # definition byte 2g
+                hi_byte = c[:, :, u, :, 16 * g + 4 * i + 2 + h].reshape(n, rg * 16)   # definition byte 2g+1
+                for s in range(4):
+                    out[:, :, 32 * b + 8 * g + s] = d * ((lo_byte >> (2 * s)) & 3) + m
+                    out[:, :, 32 * b + 8 * g + 4 + s] = d * ((hi_byte >> (2 * s)) & 3) + m
+    # rows that pad the last group hold zeros
+    assert not out[:, rows:, :].any()
+    return out[:, :rows, :].reshape(n * rows, cols)
 
 
-@pytest.mark.parametrize("fmt,rows,cols", [(1, 3, 64), (1, 2, 160), (2, 5, 96), (2, 3, 2080), (2, 2, 256),
-                                           (0, 2, 32)])
+@pytest.mark.parametrize("fmt,rows,cols", [(1, 3, 64), (1, 2, 160), (1, 37, 96), (2, 5, 96), (2, 3, 2080),
+                                           (2, 2, 256), (2, 33, 320), (0, 2, 32)])
 def test_pack_planar_is_the_documented_unit_layout(fmt, rows, cols):
     aos = synth.quant_matrices(11, 77, 2, rows, cols, fmt)
     codes, scales = moe.pack_planar(fmt, aos, 2, rows, cols)
@@ -73,19 +77,23 @@ def test_pack_planar_is_the_documented_unit_layout(fmt, rows, cols):
     got = decode_planar(fmt, codes, scales, 2, rows, cols)
     ref = oracle.dequant_rows(fmt, aos.reshape(2 * rows, -1), cols)
     assert np.array_equal(got, ref)
-    if fmt == 1 and (cols // 32) % 2:        # scale padding is zero
-        assert not scales.view(np.uint16).reshape(2 * rows, -1)[:, -1].any()
-    if fmt == 2 and (cols // 32) % 8:        # padding blocks of a row's last unit are zero, codes and scales
-        sc = scales.view(np.uint16).reshape(2 * rows, 2, -1)
-        assert not sc[:, :, cols // 32:].any()
-        rb = (cols // 32 + 7) // 8 * 64
-        nb = cols // 32
-        c = codes.reshape(2 * rows, rb)
-        for b in range(nb, (nb + 7) // 8 * 8):
-            i, h = (b % 8) // 2, b % 2
+    nb = cols // 32
+    rg = (rows + 15) // 16
+    if fmt == 1 and nb % 2:                  # scale and code padding of a row's last unit is zero
+        nu = (nb + 1) // 2
+        assert not scales.view(np.uint16).reshape(2, rg, nu, 16, 2)[:, :, -1, :, 1].any()
+        c = codes.reshape(2, rg, nu, 16, 4, 16)
+        assert not c[:, :, -1, :, :, 8:].any()
+    if fmt == 2 and nb % 8:                  # padding blocks of a row's last unit are zero, codes and scales
+        nu = (nb + 7) // 8
+        sc = scales.view(np.uint16).reshape(2, rg, nu, 2, 16, 8)
+        assert not sc[:, :, -1, :, :, nb % 8:].any()
+        c = codes.reshape(2, rg, nu, 16, 64)
+        for k in range(nb % 8, 8):
+            i, h = k // 2, k % 2
             for g in range(4):
-                w = (b // 8) * 64 + g * 16 + i * 4
-                assert not c[:, w + h].any() and not c[:, w + 2 + h].any()
+                assert not c[:, :, -1, :, 16 * g + 4 * i + h].any()
+                assert not c[:, :, -1, :, 16 * g + 4 * i + 2 + h].any()
 
 
 def test_lpt_matches_oracle():
