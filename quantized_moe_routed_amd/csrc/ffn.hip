@@ -98,6 +98,19 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
     }
   };
   if (u_beg < u_end) load_chunk(u_beg);   // the first weight loads go out before the activation set-up
+  // m values of a group of up to 4 of this wave's units (lane group g: unit ug + g), the first group's
+  // fetched now with the codes
+  uint4 mv[kNT][NM];
+  auto load_m = [&](int ug) {
+    const int u = ug + g;
+    const bool in = u < u_end;
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt)
+        mv[nt][mt] = in ? *reinterpret_cast<const uint4*>(dp(nt, mt, u) + 256u) : zero;
+  };
+  if constexpr (Codes<F>::kHasM) load_m(u_beg);
 
   // operand rows: tokens (gate/up) or grouped positions (down)
   if (tid < 16) {
@@ -135,24 +148,29 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   const uint16_t* ps = (c16 < 4 ? a.s_hi : a.s_lo) + (int64_t)arow * a.nb32;
   // m-term operands of a group of up to 4 of this wave's units (lane group g: unit ug + g): the m
   // values of the lane's column and the block sums of the slots (rows 0..3 hi, 4..7 lo)
-  uint4 mv[kNT][NM], sv = zero;
-  auto load_mterm = [&](int ug) {
+  uint4 sv = zero;
+  auto load_s = [&](int ug) {
     const int u = ug + g;
-    const bool in = u < u_end;
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-      for (int mt = 0; mt < NM; ++mt)
-        mv[nt][mt] = in ? *reinterpret_cast<const uint4*>(dp(nt, mt, u) + 256u) : zero;
-    sv = in && svalid ? *reinterpret_cast<const uint4*>(ps + UB * u) : zero;
+    sv = u < u_end && svalid ? *reinterpret_cast<const uint4*>(ps + UB * u) : zero;
   };
-
   f32x4_t acc[kNT][NM];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt) acc[nt][mt] = zero4;
   const uint32_t k1024v = to_vgpr(a.kc.k1024);
+  // m-term (2-bit blocks only): sum_b m_b (sigma S_b) over the wave's own units, four units (32
+  // blocks) per product, the first group before the main loop (its m values are already in flight)
+  auto mterm = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt) acc[nt][mt] = mfma16(sv, mv[nt][mt], acc[nt][mt]);   // sigma * value units
+  };
+  if constexpr (Codes<F>::kHasM) {
+    load_s(u_beg);
+    mterm();
+  }
 
   // main loop over this wave's code units; activations from LDS
   {
@@ -187,15 +205,12 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
       }
     }
   }
-  // m-term over the block index (2-bit blocks only): each wave adds sum_b m_b (sigma S_b) over its
-  // own units, four units (32 blocks) per product
+  // m-term of the remaining groups (more than 4 units per wave)
   if constexpr (Codes<F>::kHasM) {
-    for (int ug = u_beg; ug < u_end; ug += 4) {
-      load_mterm(ug);
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < NM; ++mt) acc[nt][mt] = mfma16(sv, mv[nt][mt], acc[nt][mt]);   // sigma * value units
+    for (int ug = u_beg + 4; ug < u_end; ug += 4) {
+      load_m(ug);
+      load_s(ug);
+      mterm();
     }
   }
   // partial sums of the four waves, added in wave order (the staging area is reused)
