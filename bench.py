@@ -76,10 +76,13 @@ def input_pool(wl, n_batches, torch):
     return [xs[i * T:(i + 1) * T] for i in range(n_batches)], toks
 
 
+LARGE_MIN = 16   # experts with this many slots or more run on the large-tile kernel (batches of 16+ tokens)
+
+
 def time_layer(layer, xs, steps, warmup, kernel, torch):
     """Run warmup + steps layer calls cycling through xs; returns the step time
-    (ms), the average duration of `kernel` (ms), and the mean number of owned
-    experts touched and of owned slots per batch."""
+    (ms), the average duration of `kernel` (ms), and per batch the mean number
+    of owned experts and of slots on small tiles and on large tiles."""
     import quantized_moe_routed_amd as moe
     from quantized_moe_routed_amd.layer import act_code
     b = layer.buffers(xs[0].shape[0], act_code(xs[0]))
@@ -98,18 +101,44 @@ def time_layer(layer, xs, steps, warmup, kernel, torch):
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / steps
     kms = trace.times_ms()
-    # per-step loads, outside the timed region: replay the routing of each batch and
-    # count the owned experts touched and the owned slots
-    owned = None if layer.g2l is None else (layer.g2l >= 0)
-    distinct, slots = [], []
+    # per-step loads, outside the timed region: replay the routing of each batch and count the
+    # owned experts and slots on each kind of tile
+    T = xs[0].shape[0]
+    large_min = LARGE_MIN if T >= LARGE_MIN else 1 << 30
+    owned = None if layer.g2l is None else (layer.g2l >= 0).cpu().numpy()
+    d_small, s_small, d_large, s_large = [], [], [], []
     for i in range(min(steps, len(xs))):
         layer.route(xs[(warmup + i) % len(xs)], b)
         layer.group(b)
-        c = b.counts if owned is None else b.counts * owned
-        distinct.append(int(torch.count_nonzero(c).item()))
-        slots.append(int(c.sum().item()))
+        c = b.counts.cpu().numpy()
+        if owned is not None:
+            c = c * owned
+        small = (c > 0) & (c < large_min)
+        d_small.append(int(small.sum()))
+        s_small.append(int(c[small].sum()))
+        d_large.append(int((c >= large_min).sum()))
+        s_large.append(int(c[c >= large_min].sum()))
     torch.cuda.synchronize()
-    return ms_step, float(np.mean(kms)), float(np.mean(distinct)), float(np.mean(slots))
+    return (ms_step, float(np.mean(kms)), float(np.mean(d_small)), float(np.mean(s_small)), float(np.mean(d_large)),
+            float(np.mean(s_large)))
+
+
+def traffic_record(kernel):
+    """HBM bytes per launch of `kernel` measured with hardware counters (profiles/), or None when
+    the kernel's source has changed since they were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return rec if h.hexdigest() == rec["sources_sha256"] else None
 
 
 def measure(name, steps, warmup, torch):
@@ -123,37 +152,43 @@ def measure(name, steps, warmup, torch):
     per_expert = layer.expert_bytes() // layer.E_local
     gateup_per_expert = (layer.gate.nbytes() + layer.up.nbytes()) // layer.E_local
     bf16 = wl.cfg.act == "bf16"
-    kernel = "ffn_gateup"
+    kernel = "ffn_gateup_large" if name == "prefill" else "ffn_gateup"
     log(f"{name}: timing {steps} steps")
-    ms, kms, D_owned, owned_slots = time_layer(layer, xs, steps, warmup, kernel, torch)
+    ms, kms, d_small, s_small, d_large, s_large = time_layer(layer, xs, steps, warmup, kernel, torch)
+    slots = s_small + s_large
     router_bytes = layer.router.nbytes()
     x_bytes = T * H * (2 if bf16 else 4)
-    layer_bytes = D_owned * per_expert + router_bytes + x_bytes + T * H * 4
-    flops = 6.0 * H * I * owned_slots
+    flops = 6.0 * H * I * slots
+    # whole-layer bytes: every touched owned expert's weights, the router, x in and the output
+    layer_bytes = (d_small + d_large) * per_expert + router_bytes + x_bytes + T * H * 4
     res = {
         "tokens_per_s": T / (ms * 1e-3),
         "ms_per_step": ms,
         "T": T,
-        "distinct_experts": D_owned,
-        "owned_slots": owned_slots,
+        "owned_slots": slots,
+        "distinct_experts": d_small + d_large,
+        "small_tile_experts": d_small,
+        "small_tile_slots": s_small,
+        "large_tile_slots": s_large,
         "layer_bytes": layer_bytes,
         "layer_gbs": layer_bytes / (ms * 1e-3) / 1e9,
         "layer_tflops": flops / (ms * 1e-3) / 1e12,
         "mfma_frac_of_bf16_peak": (flops / (ms * 1e-3) / 1e12) / BF16_PEAK_TFLOPS if bf16 else None,
-        "kernel": kernel,
-        "kernel_avg_ms": kms,
     }
-    if bf16:
-        # gate/up: 2 matrices x 2 flops x H x I per owned slot
-        kflops = 4.0 * H * I * owned_slots
+    if name == "prefill":
+        # large-tile gate/up: 2 matrices x 2 flops x H x I per slot on large tiles
+        kflops = 4.0 * H * I * s_large
         res["roofline"] = {"bound": "mfma", "achieved": kflops / (kms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": kflops / (kms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                            "traffic": None, "algorithmic_flops_per_launch": kflops}
     else:
-        # gate/up weights of the touched experts, x once per owned slot, h written once per slot
-        kbytes = D_owned * gateup_per_expert + owned_slots * (H * 4 + I * 4)
+        # small-tile gate/up: the gate/up weights of the experts on small tiles, per slot the
+        # fp16 activation operand read (hi + lo: 4 bytes a value) and h written (hi + lo)
+        kbytes = d_small * gateup_per_expert + s_small * (H * 4 + I * 4)
+        rec = traffic_record(kernel + ":" + name)
         res["roofline"] = {"bound": "hbm", "achieved": kbytes / (kms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": kbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                           "unit": "GB/s", "frac": kbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "traffic": rec["bytes_per_launch"] if rec else None,
                            "algorithmic_bytes_per_launch": kbytes}
     res["roofline"]["kernel"] = kernel
     res["roofline"]["avg_launch_ms"] = kms
@@ -180,6 +215,67 @@ def cpu_baseline(budget_s=15.0, max_tokens=400):
                       f"in {dt:.1f} s"}
 
 
+# Kernels whose HBM traffic is recorded from hardware counters, by workload, with the sources that
+# define them (the record is ignored once any of them changes).
+TRAFFIC_KERNELS = {
+    "decode": ("ffn_gateup", "moe::ffn_small_kernel<2, 2, true, 0, true>",
+               ["quantized_moe_routed_amd/csrc/ffn.hip", "quantized_moe_routed_amd/csrc/ffn.h",
+                "quantized_moe_routed_amd/csrc/fmt.h", "quantized_moe_routed_amd/csrc/device.h"]),
+}
+COPY_BYTES = 256 << 20   # the calibration copy: reads and writes this many bytes
+
+
+def calibration_copy(torch):
+    """A plain device copy of known size, for scaling the memory counters."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def record_traffic(workload, fetch_dir, write_dir):
+    """profiles/traffic.json entry for the workload's kernel, from a FETCH_SIZE run and a WRITE_SIZE
+    run of rocprofv3 (counter_collection.csv under the given directories).  Each counter is scaled
+    by what it reads for the calibration copy of COPY_BYTES."""
+    import csv
+    import glob
+    import hashlib
+    key, kname, sources = TRAFFIC_KERNELS[workload]
+
+    def per_launch(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        vals = {}
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        mine = [v for k, v in vals.items() if k.startswith("void " + kname) or k.startswith(kname)]
+        copy = [v for k, v in vals.items() if "copy" in k.lower()]
+        assert mine and copy, (counter, list(vals)[:8])
+        copy_v = max(max(v) for v in copy)   # the calibration copy (the other copies are small)
+        return float(np.mean(mine[0])), float(copy_v)
+
+    fk, fc = per_launch(fetch_dir, "FETCH_SIZE")
+    wk, wc = per_launch(write_dir, "WRITE_SIZE")
+    fetch_bytes = fk * COPY_BYTES / fc
+    write_bytes = wk * COPY_BYTES / wc
+    h = hashlib.sha256()
+    for src in sources:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    rec[key + ":" + workload] = {
+        "kernel": kname, "bytes_per_launch": fetch_bytes + write_bytes, "fetch_bytes": fetch_bytes,
+        "write_bytes": write_bytes, "fetch_counter_per_launch": fk, "write_counter_per_launch": wk,
+        "copy_fetch_counter": fc, "copy_write_counter": wc, "copy_bytes": COPY_BYTES,
+        "sources": sources, "sources_sha256": h.hexdigest()}
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps(rec[key + ":" + workload]))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,7 +285,14 @@ def main():
                     help="workload of the headline value (default: single-token decode)")
     ap.add_argument("--only", action="store_true", help="measure the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run a plain copy of known size (for scaling memory counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs (no GPU work)")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer's expert-parallel "
               "path is designed, not built, for more than one GPU)", file=sys.stderr)
@@ -198,6 +301,8 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.calibration_copy:
+        calibration_copy(torch)
     wl, head = measure(args.workload, args.steps, args.warmup, torch)
     others = {}
     if not args.only:
