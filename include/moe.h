@@ -41,8 +41,9 @@
  *    call returns a non-zero moe_status, launches nothing, leaves every output
  *    unmodified, and moe_last_error() describes the problem (thread-local).
  *  - T = 0 is a successful no-op.  There are no environment switches and no
- *    fallback paths: the activation dtype selects the kernels (fp32: dequant
- *    GEMV family; bf16: grouped MFMA GEMM).
+ *    fallback paths: every expert runs on the fp16 matrix cores, on tiles of up
+ *    to 4 slots, or of up to 128 slots for experts with 16 or more slots in a
+ *    batch of 16 or more tokens.
  *  - Calls that overlap on one stream are ordered; calls sharing a workspace
  *    on different streams race.
  */
@@ -162,13 +163,13 @@ moe_status moe_group_tokens(const int32_t* ids, int32_t T, int32_t k, int32_t E,
  *   y_slot  : [T*k, H] fp32 out; row s = D_e(silu(G_e x) * U_e x) for owned
  *             slots, rows of unowned slots are left untouched.
  * E_local must equal local->n_experts; the table's consistency is checked once
- * on the host with moe_plan_check().  fp32 activations run the dequant-GEMV
- * kernels (gate/up Q8_0 or Q2SM, down Q8_0 or Q2SM).  bf16 activations run the
- * grouped bf16 MFMA GEMM: it needs Q2SM gate/up, a Q8_0 down projection and H, I
- * multiples of 64 (else MOE_ERR_UNSUPPORTED); weight codes enter the matrix
- * cores exactly, block scales are applied in fp32 per 32-block, and the
- * intermediate silu(g)*u enters the down projection as a bf16 hi/lo pair
- * (16 significant bits).  No path uses floating-point atomics.
+ * on the host with moe_plan_check().  Every product runs on the fp16 matrix
+ * cores: weight codes enter them as exact small integers, block scales are
+ * applied in fp32 per 32-block, the activations enter as an fp16 hi + lo pair
+ * (fp32 x, 22 significant bits) or one fp16 plane (bf16 x), each token scaled
+ * by a power of two, and the intermediate silu(g)*u enters the down projection
+ * as an fp16 hi + lo pair (it must stay below 65504 in magnitude).  No path
+ * uses floating-point atomics; results do not depend on scheduling.
  * Limits: H and I multiples of 32, H <= 8192, I <= 8192. */
 moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, int32_t I, int32_t k,
                               const moe_experts* local, const int32_t* g2l, int32_t E, int32_t E_local,
@@ -187,8 +188,8 @@ moe_status moe_combine(const float* y_slot, const float* w, const int32_t* ids, 
  * While set (on the calling thread), the i-th launch of the kernel called
  * `name` gets hipEventRecord(start[i]) before and hipEventRecord(stop[i])
  * after it on the call's stream, for i < n; *count holds how many launches
- * were recorded.  Kernel names: route_logits, route_topk, group, active,
- * gemv_gateup, gemv_down, block_sums, gemm_tiles, gemm_gateup, gemm_down,
+ * were recorded.  Kernel names: route_logits, route_topk, group, prep,
+ * ffn_gateup, ffn_down (small tiles), ffn_gateup_large, ffn_down_large,
  * combine.  The caller owns the events and must keep
  * them, and count, alive while tracing; n <= 0 switches tracing off. */
 moe_status moe_trace_kernel(const char* name, hipEvent_t* start, hipEvent_t* stop, int32_t n, int32_t* count);

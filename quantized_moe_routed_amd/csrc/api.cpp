@@ -115,7 +115,7 @@ struct TilePlan {
 TilePlan tile_plan(int T, int H, int I, int k, int E_local) {
   const int64_t slots = (int64_t)T * k;
   TilePlan p{};
-  const bool large = T >= kLargeMin && H % 64 == 0 && I % 64 == 0;
+  const bool large = T >= kLargeMin;
   p.large_min = large ? kLargeMin : 0x7FFFFFFF;
   p.max_small = (int)max_tiles(slots, std::min<int64_t>(E_local, slots), kSmallTile);
   p.max_large = large ? (int)max_tiles(slots, std::min<int64_t>(E_local, slots / kLargeMin), kLargeTile) : 0;

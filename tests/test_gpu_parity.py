@@ -239,6 +239,9 @@ _LARGE_CASES = {
     "bf16_q8_q2sm": (48, 192, 8, 256, 3, dict(gate_fmt=1, up_fmt=1, down_fmt=2, router_fmt=1, act="bf16")),
     # several full tiles of 128 slots per expert plus ragged tails, next to one small expert
     "f32_multi_tile": (300, 128, 4, 128, 2, dict(gate_fmt=2, up_fmt=2, down_fmt=1, router_fmt=1, act="f32")),
+    # an odd number of blocks per row (H = 2080: 65 blocks), I = 96 (a partial column tile and a
+    # partly filled 2-bit unit in the down projection)
+    "f32_odd_blocks": (40, 2080, 4, 96, 2, dict(gate_fmt=1, up_fmt=1, down_fmt=2, router_fmt=1, act="f32")),
 }
 
 
