@@ -125,7 +125,7 @@ TilePlan tile_plan(int T, int H, int I, int k, int E_local) {
 int pad32(int nb) { return (nb + 31) / 32 * 32; }
 
 struct FwdLayout {
-  size_t n_small, n_large, small, large, sigma, xq_hi, xq_lo, sq_hi, sq_lo, h_hi, h_lo, hs_hi, hs_lo, total;
+  size_t n_small, n_large, small, small_tok, large, sigma, xq_hi, xq_lo, sq_hi, sq_lo, h_hi, h_lo, hs_hi, hs_lo, total;
 };
 
 FwdLayout fwd_layout(int T, int H, int I, int k, int E_local, int xt) {
@@ -142,6 +142,7 @@ FwdLayout fwd_layout(int T, int H, int I, int k, int E_local, int xt) {
   L.n_small = take(sizeof(int32_t));
   L.n_large = take(sizeof(int32_t));
   L.small = take((size_t)tp.max_small * 4 * sizeof(int32_t));
+  L.small_tok = take((size_t)tp.max_small * 4 * sizeof(int32_t));
   L.large = take((size_t)tp.max_large * 4 * sizeof(int32_t));
   L.sigma = take((size_t)T * sizeof(float));
   L.xq_hi = take((size_t)T * H * 2);
@@ -349,6 +350,7 @@ moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, i
   a.down = qm(local->down);
   a.slot_list = slot_list;
   a.small = reinterpret_cast<const int4*>(wsb + L.small);
+  a.small_tok = reinterpret_cast<const int4*>(wsb + L.small_tok);
   a.large = reinterpret_cast<const int4*>(wsb + L.large);
   a.n_small = reinterpret_cast<const int32_t*>(wsb + L.n_small);
   a.n_large = reinterpret_cast<const int32_t*>(wsb + L.n_large);
@@ -377,6 +379,9 @@ moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, i
   tl.bm_large = kLargeTile;
   tl.max_large = tp.max_large;
   tl.small = reinterpret_cast<int4*>(wsb + L.small);
+  tl.small_tok = reinterpret_cast<int4*>(wsb + L.small_tok);
+  tl.slot_list = slot_list;
+  tl.k = k;
   tl.large = reinterpret_cast<int4*>(wsb + L.large);
   tl.n_small = reinterpret_cast<int32_t*>(wsb + L.n_small);
   tl.n_large = reinterpret_cast<int32_t*>(wsb + L.n_large);

@@ -16,6 +16,7 @@ struct FfnTileArgs {
   QMat w0, w1;                      // gate, up (gate/up) or down (w0 only)
   const int32_t* slot_list;
   const int4* tiles;
+  const int4* tile_tok;             // small gate/up tiles: the token of each row
   const int32_t* n_tiles;
   int fd, I, nb32I;                 // gate/up: down format, I, padded block count of h
   int stage_rows;                   // small tiles: rows of the LDS staging area (min(4, T))
@@ -44,6 +45,15 @@ __device__ __forceinline__ float d_of(const uint4& dw, int i) {
   }
   return half_bits_to_float((i & 1) ? (w >> 16) : (w & 0xFFFFu)) * kScaleD;
 }
+
+// Direct load of 16 bytes per lane into LDS: lane l's bytes land at lds_base + 16 l (lanes off in
+// EXEC load nothing).  Completion is tracked by vmcnt only; the compiler does not see these loads,
+// so the caller waits for them explicitly before reading the LDS.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Large-tile launch (ffn_large.hip): tiles of up to 128 slots of one expert.
 hipError_t launch_large(const FfnTileArgs& t, int fmt, int mode, bool lo, int max_tiles, hipStream_t s);

@@ -43,12 +43,14 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   constexpr int CH = NM == 2 ? 2 : (F == FMT_Q8_0 ? 4 : 1);   // units whose loads are issued together
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ float s_sig[16];
-  __shared__ int32_t s_row[16];
 
   const int tile = blockIdx.y;
   if (tile >= *a.n_tiles) return;
   const int4 tl = a.tiles[tile];
   const int le = tl.x, p0 = tl.y, rows = tl.z;
+  // operand rows of the tile: tokens (gate/up, listed with the tile) or grouped positions (down)
+  const int4 tk = MODE == MODE_GATEUP ? a.tile_tok[tile] : make_int4(p0, p0 + 1, p0 + 2, p0 + 3);
+  auto row_of = [&](int m) { return m == 0 ? tk.x : m == 1 ? tk.y : m == 2 ? tk.z : tk.w; };
   const int n0 = blockIdx.x * 16 * kNT;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int c16 = lane & 15, g = lane >> 4;
@@ -97,7 +99,30 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
         }
     }
   };
-  if (u_beg < u_end) load_chunk(u_beg);   // the first weight loads go out before the activation set-up
+  // Each wave moves its own slice of the tile's activation rows (the values of its code units) to
+  // LDS with direct loads, ahead of its codes so that they are not queued behind the weight stream;
+  // no other wave reads that slice, so no barrier is needed before the main loop.
+  uint16_t* st_hi = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* st_lo = st_hi + a.stage_rows * K;
+  uint16_t* st_zero = st_lo + (LO ? a.stage_rows * K : 0);   // one row of zeros for rows without a slot
+  if (tid < kStageRows) s_sig[tid] = MODE == MODE_GATEUP && tid < rows ? a.sigma[row_of(tid)] : kSigmaH;
+  {
+    const int k0 = 32 * UB * u_beg, k1 = min(32 * UB * u_end, K);
+    for (int e = k0 + 8 * lane; e < k1; e += 8 * kWave)
+      *reinterpret_cast<uint4*>(st_zero + e) = make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    for (int pl = 0; pl < (LO ? 2 : 1); ++pl)
+      for (int m = 0; m < rows; ++m)
+        for (int c0 = k0; c0 < k1; c0 += 512) {   // 1 KiB per instruction
+          const int e = c0 + 8 * lane;
+          if (e < k1) {
+            const uint16_t* src = (pl ? a.a_lo : a.a_hi) + (int64_t)row_of(m) * K + e;
+            const uint32_t dst = lds0 + (uint32_t)((((pl ? a.stage_rows : 0) + m) * K + c0) * 2);
+            dma16(src, __builtin_amdgcn_readfirstlane(dst));
+          }
+        }
+  }
+  if (u_beg < u_end) load_chunk(u_beg);
   // m values of a group of up to 4 of this wave's units (lane group g: unit ug + g), the first group's
   // fetched now with the codes
   uint4 mv[kNT][NM];
@@ -112,36 +137,10 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   };
   if constexpr (Codes<F>::kHasM) load_m(u_beg);
 
-  // operand rows: tokens (gate/up) or grouped positions (down)
-  if (tid < 16) {
-    int r = 0;
-    float sg = kSigmaH;
-    if (tid < rows) {
-      r = MODE == MODE_GATEUP ? a.slot_list[p0 + tid] / a.k : p0 + tid;
-      if (MODE == MODE_GATEUP) sg = a.sigma[r];
-    }
-    s_row[tid] = r;
-    s_sig[tid] = sg;
-  }
-  uint16_t* st_hi = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* st_lo = st_hi + a.stage_rows * K;
-  uint16_t* st_zero = st_lo + (LO ? a.stage_rows * K : 0);   // one row of zeros for rows without a slot
-  for (int j = tid; j < K / 8; j += kFfnThreads) reinterpret_cast<uint4*>(st_zero)[j] = make_uint4(0u, 0u, 0u, 0u);
-  __syncthreads();
-  {
-    const int per_row = K / 8;
-    for (int j = tid; j < rows * per_row; j += kFfnThreads) {
-      const int m = j / per_row, c = j % per_row;
-      const int64_t src = (int64_t)s_row[m] * K + 8 * c;
-      reinterpret_cast<uint4*>(st_hi)[m * per_row + c] = *reinterpret_cast<const uint4*>(a.a_hi + src);
-      if (LO) reinterpret_cast<uint4*>(st_lo)[m * per_row + c] = *reinterpret_cast<const uint4*>(a.a_lo + src);
-    }
-    __syncthreads();
-  }
   // A fragment rows: 0..3 the hi plane of slots 0..3, 4..7 their lo plane, 8..15 zero
   const int slot_m = c16 & 3;
   const bool mvalid = slot_m < rows && (c16 < 4 || (LO && c16 < 8));
-  const int arow = s_row[slot_m < rows ? slot_m : 0];
+  const int arow = row_of(slot_m < rows ? slot_m : 0);
   const uint16_t* pa = (mvalid ? (c16 < 4 ? st_hi : st_lo) + slot_m * K : st_zero) + 8 * g;
   // the m-term operand: rows 0..3 hi, 4..7 lo of the block sums
   const bool svalid = slot_m < rows && c16 < 8;
@@ -153,6 +152,9 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
     const int u = ug + g;
     sv = u < u_end && svalid ? *reinterpret_cast<const uint4*>(ps + UB * u) : zero;
   };
+  if constexpr (Codes<F>::kHasM) load_s(u_beg);
+  // every load of this wave is in flight; its slice of rows and its first codes are needed first
+  wait_vmem();
   f32x4_t acc[kNT][NM];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt)
@@ -167,10 +169,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
 #pragma unroll
       for (int mt = 0; mt < NM; ++mt) acc[nt][mt] = mfma16(sv, mv[nt][mt], acc[nt][mt]);   // sigma * value units
   };
-  if constexpr (Codes<F>::kHasM) {
-    load_s(u_beg);
-    mterm();
-  }
+  if constexpr (Codes<F>::kHasM) mterm();
 
   // main loop over this wave's code units; activations from LDS
   {
@@ -325,7 +324,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   const bool one = a.T == 1;
 #define MOE_SMALL(F, NM, LO, MODE) \
   (one ? launch_small_t<F, NM, LO, MODE, true>(t, a.max_small, s) : launch_small_t<F, NM, LO, MODE, false>(t, a.max_small, s))
-  t.tiles = a.small; t.n_tiles = a.n_small;
+  t.tiles = a.small; t.tile_tok = a.small_tok; t.n_tiles = a.n_small;
   trace_pre("ffn_gateup", s);
   if (a.fg == FMT_Q2SM)
     err = lo ? MOE_SMALL(FMT_Q2SM, 2, true, MODE_GATEUP) : MOE_SMALL(FMT_Q2SM, 2, false, MODE_GATEUP);

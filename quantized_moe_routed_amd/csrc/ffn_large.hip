@@ -43,14 +43,6 @@ __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
 
 constexpr int kLgRows = 128;      // slots per tile
 
-// Direct load of 16 bytes per lane into LDS: lane l's bytes land at lds_base + 16 l.
-// Completion is tracked by vmcnt only (waited for explicitly before the barrier).
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // Value barriers: the computation of v stays ahead of every later volatile asm statement.
 __device__ __forceinline__ void pin(uint4& v) {
   u32x4_t t = __builtin_bit_cast(u32x4_t, v);

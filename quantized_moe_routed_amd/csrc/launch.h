@@ -30,6 +30,9 @@ struct TileLists {
   int bm_small, max_small, bm_large, max_large;
   int4 *small, *large;
   int32_t *n_small, *n_large;
+  int4* small_tok;              // tokens of the rows of each small tile (bm_small <= 4)
+  const int32_t* slot_list;
+  int k;
 };
 
 // Arguments of the expert FFN launches (workspace pointers included).
@@ -38,6 +41,7 @@ struct FfnArgs {
   QMat gate, up, down;
   const int32_t* slot_list;
   const int4 *small, *large;
+  const int4* small_tok;
   const int32_t *n_small, *n_large;
   int max_small, max_large;   // max_large = 0: no large tiles can exist
   const uint16_t *xq_hi, *xq_lo, *sq_hi, *sq_lo;

@@ -26,10 +26,14 @@ __device__ __forceinline__ float act_at(const void* x, int64_t i) {
 // received slots, in ascending global id: tile i covers grouped positions
 // p0 .. p0+rows-1 of local expert .x.  Tiles past max_tiles, and rows past the
 // n_slots grouped positions, are never produced, whatever the counts hold.
+// With tok != NULL (tiles of up to 4 slots), tok[i] also receives the token of each row of tile i
+// (slot / k; 0 for rows past the tile), so that the expert kernel can fetch the tile's activation
+// rows without first reading the slot list.
 __device__ void build_tiles(const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
                             const int32_t* __restrict__ g2l, int E, int E_local, int n_slots, int bm, int lo_n,
                             int hi_n, int max_tiles, int4* __restrict__ tiles, int32_t* __restrict__ n_tiles,
-                            int32_t* wave_tot) {
+                            int32_t* wave_tot, int4* __restrict__ tok = nullptr,
+                            const int32_t* __restrict__ slot_list = nullptr, int k = 1) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   int n = 0, mt = 0, l = -1, p = 0;
   if (tid < E) {
@@ -50,8 +54,16 @@ __device__ void build_tiles(const int32_t* __restrict__ counts, const int32_t* _
   int base = 0;
   for (int w = 0; w < wave; ++w) base += wave_tot[w];
   base += incl - mt;
-  for (int i = 0; i < mt && base + i < max_tiles; ++i)
-    tiles[base + i] = make_int4(l, p + bm * i, min(bm, n - bm * i), tid);
+  for (int i = 0; i < mt && base + i < max_tiles; ++i) {
+    const int rows = min(bm, n - bm * i);
+    tiles[base + i] = make_int4(l, p + bm * i, rows, tid);
+    if (tok) {
+      int r[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = j < rows ? slot_list[p + bm * i + j] / k : 0;
+      tok[base + i] = make_int4(r[0], r[1], r[2], r[3]);
+    }
+  }
   if (tid == 0) {
     int tot = 0;
     for (int w = 0; w < kPrepThreads / kWave; ++w) tot += wave_tot[w];
@@ -122,7 +134,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const void* __restri
   __shared__ int32_t wave_tot[kPrepThreads / kWave];
   if (blockIdx.x == 0) {
     build_tiles(tl.counts, tl.offsets, tl.g2l, tl.E, tl.E_local, tl.n_slots, tl.bm_small, 1, tl.large_min,
-                tl.max_small, tl.small, tl.n_small, wave_tot);
+                tl.max_small, tl.small, tl.n_small, wave_tot, tl.small_tok, tl.slot_list, tl.k);
     build_tiles(tl.counts, tl.offsets, tl.g2l, tl.E, tl.E_local, tl.n_slots, tl.bm_large, tl.large_min, 0x7FFFFFFF,
                 tl.max_large, tl.large, tl.n_large, wave_tot);
   } else {
