@@ -43,7 +43,7 @@ __device__ __forceinline__ float d_of(const uint4& dw, int i) {
   } else {
     w = dw.x;
   }
-  return half_bits_to_float((i & 1) ? (w >> 16) : (w & 0xFFFFu)) * kScaleD;
+  return half_bits_to_float((i & 1) ? (w >> 16) : (w & 0xFFFFu)) * Codes<F>::kDScale;
 }
 
 // Direct load of 16 bytes per lane into LDS: lane l's bytes land at lds_base + 16 l (lanes off in
@@ -54,6 +54,12 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                : "memory", "m0");
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_at_most() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Large-tile launch (ffn_large.hip): tiles of up to 128 slots of one expert.
 hipError_t launch_large(const FfnTileArgs& t, int fmt, int mode, bool lo, int max_tiles, hipStream_t s);

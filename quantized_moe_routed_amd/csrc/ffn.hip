@@ -122,18 +122,22 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
           }
         }
   }
-  if (u_beg < u_end) load_chunk(u_beg);
-  // m values of a group of up to 4 of this wave's units (lane group g: unit ug + g), the first group's
-  // fetched now with the codes
+  // m values of a group of up to 4 of this wave's units (lane group g: unit ug + g); the first
+  // group's m values and block sums are fetched right after the row slices, ahead of the codes
   uint4 mv[kNT][NM];
+  // (every load is issued, from a clamped unit, and its value dropped when out of range: no load
+  // sits behind a branch, so the loads issued after the row slices are known)
   auto load_m = [&](int ug) {
     const int u = ug + g;
     const bool in = u < u_end;
+    const int uc = min(u, n_units - 1);
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-      for (int mt = 0; mt < NM; ++mt)
-        mv[nt][mt] = in ? *reinterpret_cast<const uint4*>(dp(nt, mt, u) + 256u) : zero;
+      for (int mt = 0; mt < NM; ++mt) {
+        const uint4 v = *reinterpret_cast<const uint4*>(dp(nt, mt, uc) + 256u);
+        mv[nt][mt] = in ? v : zero;
+      }
   };
   if constexpr (Codes<F>::kHasM) load_m(u_beg);
 
@@ -150,19 +154,23 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   uint4 sv = zero;
   auto load_s = [&](int ug) {
     const int u = ug + g;
-    sv = u < u_end && svalid ? *reinterpret_cast<const uint4*>(ps + UB * u) : zero;
+    const uint4 v = *reinterpret_cast<const uint4*>(ps + UB * min(u, n_units - 1));
+    sv = u < u_end && svalid ? v : zero;
   };
   if constexpr (Codes<F>::kHasM) load_s(u_beg);
-  // every load of this wave is in flight; its slice of rows and its first codes are needed first
-  wait_vmem();
+  load_chunk(u_beg);
+  // Every load of this wave is in flight.  Loads complete in issue order, so once no more than the
+  // chunk's code and scale loads (issued last) are outstanding, the slices are in LDS and the m-term operands in registers; the codes
+  // themselves are waited for where they are used.
+  wait_vmem_at_most<CH * kNT * NM * 2>();
   f32x4_t acc[kNT][NM];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt) acc[nt][mt] = zero4;
-  const uint32_t k1024v = to_vgpr(a.kc.k1024);
+
   // m-term (2-bit blocks only): sum_b m_b (sigma S_b) over the wave's own units, four units (32
-  // blocks) per product, the first group before the main loop (its m values are already in flight)
+  // blocks) per product, the first group before the main loop
   auto mterm = [&]() {
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt)
@@ -171,33 +179,37 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   };
   if constexpr (Codes<F>::kHasM) mterm();
 
-  // main loop over this wave's code units; activations from LDS
-  {
-    for (int u0 = u_beg; u0 < u_end; u0 += CH) {
-      if (u0 != u_beg) load_chunk(u0);
+  // main loop over this wave's code units, a unit as soon as its codes are in; activations from LDS
+  for (int u0 = u_beg; u0 < u_end; u0 += CH) {
+    if (u0 != u_beg) load_chunk(u0);
 #pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const int u = u0 + j;
-        if (u >= u_end) break;
+    for (int j = 0; j < CH; ++j) {
+      const int u = u0 + j;
+      if (u >= u_end) break;
 #pragma unroll
-        for (int i = 0; i < UB; ++i) {
-          const int b = u * UB + i;
-          if (b >= nb) break;
-          const uint4 av = *reinterpret_cast<const uint4*>(pa + 32 * b);
+      for (int i = 0; i < UB; ++i) {
+        const int b = u * UB + i;
+        if (b >= nb) break;
+        const uint4 av = *reinterpret_cast<const uint4*>(pa + 32 * b);
+        // per output tile: the fragments of both matrices, both products, then both folds, so
+        // that no fold waits on the product issued just before it
 #pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) {
+        for (int nt = 0; nt < kNT; ++nt) {
+          uint4 bf[NM];
+          f32x4_t p[NM];
 #pragma unroll
-            for (int mt = 0; mt < NM; ++mt) {
-              const uint4 bf = Codes<F>::frag(cw[j][nt][mt], i, a.kc, k1024v);
-              const f32x4_t p = mfma16(av, bf, zero4);
-              const float d = d_of<F>(dw[j][nt][mt], i);
-              // output row 4(l/16)+r holds slot r (hi or lo plane) for the first two lane groups
-              acc[nt][mt][0] = fmaf(d, p[0], acc[nt][mt][0]);
-              if (!ONE) {
-                acc[nt][mt][1] = fmaf(d, p[1], acc[nt][mt][1]);
-                acc[nt][mt][2] = fmaf(d, p[2], acc[nt][mt][2]);
-                acc[nt][mt][3] = fmaf(d, p[3], acc[nt][mt][3]);
-              }
+          for (int mt = 0; mt < NM; ++mt) bf[mt] = Codes<F>::frag(cw[j][nt][mt], i, a.kc);
+#pragma unroll
+          for (int mt = 0; mt < NM; ++mt) p[mt] = mfma16(av, bf[mt], zero4);
+#pragma unroll
+          for (int mt = 0; mt < NM; ++mt) {
+            const float d = d_of<F>(dw[j][nt][mt], i);
+            // output row 4(l/16)+r holds slot r (hi or lo plane) for the first two lane groups
+            acc[nt][mt][0] = fmaf(d, p[mt][0], acc[nt][mt][0]);
+            if (!ONE) {
+              acc[nt][mt][1] = fmaf(d, p[mt][1], acc[nt][mt][1]);
+              acc[nt][mt][2] = fmaf(d, p[mt][2], acc[nt][mt][2]);
+              acc[nt][mt][3] = fmaf(d, p[mt][3], acc[nt][mt][3]);
             }
           }
         }
@@ -257,10 +269,9 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
         h = silu(gs * inv) * (us * inv);
         const int col = n0 + cl;
         const int blk = col >> 5, kk = col & 31, gg = kk >> 3;
-        const int e = elem_of_rt(a.fd, kk & 7);
-        const float hv = h * ldexpf(1.0f, -pos_rt(a.fd, e));   // kSigmaH * 2^(6 - pos)
+        const int e = frag_val(kk & 7);
         uint32_t hi, lo;
-        split_f16(hv, hi, lo);
+        split_f16(h, hi, lo);   // h * kSigmaH * 2^6
         const int64_t at = (int64_t)(p0 + m) * a.I + 32 * blk + 8 * gg + e;
         a.h_hi[at] = (uint16_t)hi;
         a.h_lo[at] = (uint16_t)lo;

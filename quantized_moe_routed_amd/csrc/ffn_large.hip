@@ -203,7 +203,6 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
       for (int mt = 0; mt < NM; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[mi][nt][mt][e] = 0.0f;
-  const uint32_t k1024v = to_vgpr(a.kc.k1024);
   const int nbs = (nb + SB - 1) / SB * SB;   // blocks the loop runs over
   const int n_st = nbs / SB;
 
@@ -271,8 +270,8 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
       for (int nt = 0; nt < NT2; ++nt)
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt) {
-          bf0[nt][mt][0] = Codes<F>::frag(cw[0][nt][mt][0], 0, a.kc, k1024v);
-          bf0[nt][mt][1] = Codes<F>::frag(cw[0][nt][mt][1], 0, a.kc, k1024v);
+          bf0[nt][mt][0] = Codes<F>::frag(cw[0][nt][mt][0], 0, a.kc);
+          bf0[nt][mt][1] = Codes<F>::frag(cw[0][nt][mt][1], 0, a.kc);
           d0[nt][mt] = d_of<F>(dw[0][nt][mt], 0);
           // pinned here, ahead of the activation loads below
           pin(bf0[nt][mt][0]);
@@ -298,8 +297,8 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
               bf[nt][mt][1] = bf0[nt][mt][1];
               d[nt][mt] = d0[nt][mt];
             } else {
-              bf[nt][mt][0] = Codes<F>::frag(cw[j][nt][mt][0], ib, a.kc, k1024v);
-              bf[nt][mt][1] = Codes<F>::frag(cw[j][nt][mt][1], ib, a.kc, k1024v);
+              bf[nt][mt][0] = Codes<F>::frag(cw[j][nt][mt][0], ib, a.kc);
+              bf[nt][mt][1] = Codes<F>::frag(cw[j][nt][mt][1], ib, a.kc);
               d[nt][mt] = d_of<F>(dw[j][nt][mt], ib);
             }
           }
@@ -395,9 +394,9 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
         if (valid && colv[0]) {
           const float inv = s_inv[row];
           h = silu(acc[mi][0][0][e] * inv) * (acc[mi][0][1][e] * inv);
-          const int el = elem_of_rt(a.fd, c32 & 7);
+          const int el = frag_val(c32 & 7);
           uint32_t hi, lo;
-          split_f16(h * ldexpf(1.0f, -pos_rt(a.fd, el)), hi, lo);
+          split_f16(h, hi, lo);   // h * kSigmaH * 2^6
           const int64_t at = (int64_t)(p0 + row) * a.I + n0 + 8 * (c32 >> 3) + el;
           a.h_hi[at] = (uint16_t)hi;
           a.h_lo[at] = (uint16_t)lo;

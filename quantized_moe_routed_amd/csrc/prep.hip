@@ -5,7 +5,7 @@
 // Activation operand of token t for a gate/up format F (see fmt.h):
 //   sigma_t = 2^(9-E), E the smallest integer with max_i |x[t,i]| < 2^E
 //             (1 for an all-zero token), so that |x| * sigma * 2^6 < 2^15;
-//   A'[t][32b+8g+e] = x[t][32b+8g+val(e)] * sigma_t * 2^(6-pos(e))   (hi, lo)
+//   A'[t][32b+8g+e] = x[t][32b+8g+frag_val(e)] * sigma_t * 2^6        (hi, lo)
 //   S'[t][b]        = sigma_t * sum_{i<32} x[t][32b+i]               (hi, lo)
 // The block sums are taken in index order in fp32; blocks past H/32 up to
 // the padded count are zero.
@@ -103,8 +103,7 @@ __device__ void prep_token(const void* __restrict__ x, int t, int H, int nb32, u
     uint32_t hi[8], lo[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = act_at<ACT>(x, row + 32 * b + 8 * g + Codes<FMT>::val(e)) * sg *
-                      ldexpf(1.0f, 6 - Codes<FMT>::pos(e));
+      const float v = act_at<ACT>(x, row + 32 * b + 8 * g + frag_val(e)) * sg * 64.0f;
       split_f16(v, hi[e], lo[e]);
     }
     const int64_t o = row + 32 * b + 8 * g;
