@@ -95,7 +95,8 @@ thread_local Trace g_trace;
 moe::QMat qm(const moe_qmat& m) { return moe::QMat{m.codes, m.scales, m.rows, m.cols}; }
 
 // ---- workspace layouts -------------------------------------------------------
-size_t route_ws_bytes(int T, int E) { return align_up((size_t)T * E * sizeof(float)); }
+// (the size query does not know the router's format: it reports the larger, Q8_0, need)
+size_t route_ws_bytes(int T, int E, int H, int fmt = MOE_W_Q8_0) { return align_up(moe::route_ws_need(T, E, H, fmt)); }
 
 // Expert-forward workspace: tile list, per-token row scales, the fp16
 // activation operand (hi plane; lo plane for fp32 activations) with its block
@@ -214,7 +215,7 @@ moe_status moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t k, int32_
   if (T < 0 || H <= 0 || I <= 0 || k <= 0 || E <= 0 || E_local < 0 || E_local > E)
     return fail(MOE_ERR_ARG, "moe_workspace_size: bad sizes");
   if (xt != MOE_ACT_F32 && xt != MOE_ACT_BF16) return fail(MOE_ERR_ARG, "moe_workspace_size: unknown activation type");
-  if (route_ws) *route_ws = route_ws_bytes(T, E);
+  if (route_ws) *route_ws = route_ws_bytes(T, E, H);
   if (group_ws) *group_ws = 0;
   if (forward_ws) *forward_ws = fwd_layout(T, H, I, k, E_local, xt).total;
   return ok();
@@ -236,7 +237,7 @@ moe_status moe_route(const void* x, int32_t xt, int32_t T, int32_t H, const moe_
   if (k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "moe_route: k = %d exceeds %d", k, kMaxK);
   if (T > 0 && (!x || !ids || !w)) return fail(MOE_ERR_ARG, "moe_route: x, ids and w must not be NULL");
   if (!aligned16(x)) return fail(MOE_ERR_ARG, "moe_route: x must be 16-byte aligned");
-  const size_t need = route_ws_bytes(T, E);
+  const size_t need = route_ws_bytes(T, E, H, router->fmt);
   if (ws_bytes < need || (need && !ws))
     return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu bytes, need %zu", ws_bytes, need);
   if (T == 0) return ok();
@@ -250,8 +251,8 @@ moe_status moe_route(const void* x, int32_t xt, int32_t T, int32_t H, const moe_
   dc(w, "w");
   dc(ws, "workspace");
   if (dc.st) return dc.st;
-  hipError_t e = moe::launch_route(x, xt, T, H, router->fmt, qm(*router), bias, k, ids, w,
-                                   reinterpret_cast<float*>(ws), s);
+  if (!aligned16(ws)) return fail(MOE_ERR_ARG, "moe_route: workspace must be 16-byte aligned");
+  hipError_t e = moe::launch_route(x, xt, T, H, router->fmt, qm(*router), bias, k, ids, w, ws, s);
   if (e != hipSuccess) return hip_fail(e, "moe_route launch");
   return ok();
 }

@@ -14,7 +14,8 @@ void trace_pre(const char* name, hipStream_t s);
 void trace_post(const char* name, hipStream_t s);
 
 hipError_t launch_route(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
-                        int k, int32_t* ids, float* w, float* z_ws, hipStream_t s);
+                        int k, int32_t* ids, float* w, void* ws, hipStream_t s);
+size_t route_ws_need(int T, int E, int H, int fmt);   // workspace bytes of launch_route
 
 hipError_t launch_group(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
                         int32_t* slot_list, hipStream_t s);

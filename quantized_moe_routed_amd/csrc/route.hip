@@ -13,27 +13,31 @@
 // adds adjacent subtrees exactly as the tree does (IEEE addition commutes).
 // Lanes past the last block contribute +0.0: padding the tree with zeros
 // changes no value, so the result equals the carry-up tree for any block count.
+#include <type_traits>
+
 #include "device.h"
 #include "fmt.h"
 #include "launch.h"
 
 namespace moe {
 
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 constexpr int kRouteTokTile = 16;
 
-template <int FMT, int ACT, int C>
-__global__ __launch_bounds__(256) void route_logits_kernel(const void* __restrict__ x, int T, int H,
-                                                           const void* __restrict__ codes,
-                                                           const void* __restrict__ scales,
-                                                           const float* __restrict__ bias, int E,
-                                                           float* __restrict__ z) {
-  const int lane = threadIdx.x % kWave;
-  const int e = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (e >= E) return;
+// The C blocks lane*C .. lane*C+C-1 of router row e as floats (int8 codes or fp32 weights) and their
+// scales d (Q8_0; 0 for blocks past the row); blocks past nb are zero.
+template <int FMT, int C>
+__device__ __forceinline__ void load_router_blocks(const void* __restrict__ codes, const void* __restrict__ scales,
+                                                   int e, int H, int lane, float (&wv)[C][32], float (&dsc)[C]) {
   const int nb = H / 32;
-
-  float wv[C][32];
-  float dsc[C];
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     const int b = lane * C + j;
@@ -71,6 +75,38 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
       for (int i = 0; i < 32; ++i) wv[j][i] = 0.0f;
     }
   }
+}
+
+// z of one (token, expert) pair from the lane's block chains r[0..C-1]: the first log2 C levels of
+// the pairwise tree in registers, the rest an xor butterfly across the wave (every lane ends with z).
+template <int C>
+__device__ __forceinline__ float tree_sum(float (&r)[C]) {
+#pragma unroll
+  for (int w = 1; w < C; w <<= 1) {
+#pragma unroll
+    for (int j = 0; j + w < C; j += 2 * w) r[j] = r[j] + r[j + w];
+  }
+  float v = r[0];
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v = v + __shfl_xor(v, m, kWave);
+  return v;
+}
+
+
+template <int FMT, int ACT, int C>
+__global__ __launch_bounds__(256) void route_logits_kernel(const void* __restrict__ x, int T, int H,
+                                                           const void* __restrict__ codes,
+                                                           const void* __restrict__ scales,
+                                                           const float* __restrict__ bias, int E,
+                                                           float* __restrict__ z) {
+  const int lane = threadIdx.x % kWave;
+  const int e = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (e >= E) return;
+  const int nb = H / 32;
+
+  float wv[C][32];
+  float dsc[C];
+  load_router_blocks<FMT, C>(codes, scales, e, H, lane, wv, dsc);
   const float be = bias ? bias[e] : 0.0f;
 
   const int t0 = blockIdx.y * kRouteTokTile;
@@ -114,15 +150,240 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
         r[j] = (FMT == FMT_Q8_0) ? dsc[j] * p : p;
       }
     }
-#pragma unroll
-    for (int w = 1; w < C; w <<= 1) {
-#pragma unroll
-      for (int j = 0; j + w < C; j += 2 * w) r[j] = r[j] + r[j + w];
-    }
-    float v = r[0];
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) v = v + __shfl_xor(v, m, kWave);
+    const float v = tree_sum<C>(r);
     if (lane == 0) z[(int64_t)t * E + e] = bias ? v + be : v;
+  }
+}
+
+// ---- many tokens: one token per lane ------------------------------------------------------
+// For batches of kLanesMinTokens tokens or more (Q8_0 router) the logits are taken with one
+// token per lane.  Each lane keeps its own chains and its own pairwise tree in registers (no
+// cross-lane sums); the weight of a step is the same for every lane and reaches the lanes through
+// the broadcast form of a fused multiply-add: v_fmac_f32_dpp with row_newbcast:n takes its weight
+// from lane n of the lane's row of 16.  A register therefore carries 16 steps' weights of one
+// expert (lane 16 r + n holds step n), and one 4-byte load per lane (4 consecutive codes) plus
+// four conversions give the weights of 64 steps (a Q8_0 unit, two blocks): register k holds
+// steps 4 n + k.
+//
+// Workgroup: 4 waves = 4 groups of 8 experts x 64 tokens x one of S equal ranges of the blocks.
+// The tokens' activations pass through LDS in chunks of 4 blocks, stored transposed (lane t reads
+// 16 bytes of its token at slot c * 64 + (t ^ (c & 15)): conflict-free for the reads and for
+// the coalesced writes).  Each lane adds its blocks pairwise in registers: the 4 blocks of a
+// chunk, then the chunks with a binary counter (level j holds a complete subtree of 2^j
+// chunks).  A range of 2^n blocks therefore yields exactly the subtree of the canonical tree over
+// those blocks; the S subtree sums are added pairwise (the tree's top levels) by the selection
+// kernel, which then adds the bias.
+constexpr int kLanesMinTokens = 16;
+constexpr int kLaneGroup = 8;          // experts per wave
+constexpr int kLanesWaves = 4;
+constexpr int kChunkBlocks = 4;
+constexpr int kMaxChunkLevels = 7;     // up to 128 chunks (512 blocks) per range
+constexpr int kMaxRanges = 32;         // block ranges S (a power of two)
+
+struct LanesPlan {
+  bool use;
+  int S;              // block ranges
+  int groups;         // expert groups of 8
+};
+
+static LanesPlan lanes_plan(int T, int E, int H, int fmt) {
+  LanesPlan p{};
+  const int nb = H / 32;
+  p.use = fmt == FMT_Q8_0 && T >= kLanesMinTokens && nb >= kChunkBlocks && (nb & (nb - 1)) == 0;
+  if (!p.use) return p;
+  p.groups = (E + kLaneGroup - 1) / kLaneGroup;
+  const long wgs = (long)((T + 63) / 64) * ((p.groups + kLanesWaves - 1) / kLanesWaves);
+  p.S = 1;
+  while (nb / p.S > kChunkBlocks << kMaxChunkLevels) p.S <<= 1;
+  while (wgs * p.S * 2 <= 512 && nb / (p.S * 2) >= kChunkBlocks && p.S * 2 <= kMaxRanges) p.S <<= 1;
+  if (p.S > kMaxRanges) p.use = false;
+  return p;
+}
+
+size_t route_ws_need(int T, int E, int H, int fmt) {
+  const LanesPlan p = lanes_plan(T, E, H, fmt);
+  return (size_t)(p.use ? p.S : 1) * T * E * sizeof(float);
+}
+
+// p += w(lane 16 r + N) * x  (fused, one rounding).  A DPP operand must not have been written by
+// a vector instruction in the two instructions before; the compiler does not look inside inline
+// assembly, so the weights are produced by convert_codes (which ends with two wait states) and
+// the library build scans the compiled code for any such write before a broadcast.
+template <int N>
+__device__ __forceinline__ void fmac_bcast(float& p, float w, float x) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(p) : "v"(w), "v"(x), "n"(N));
+}
+
+// The four int8 codes of a word as fp32 (sign-extending byte selects), then two wait states.
+__device__ __forceinline__ void convert_codes(uint32_t w, float (&o)[4]) {
+  asm("v_cvt_f32_i32_sdwa %0, sext(%4) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+      "v_cvt_f32_i32_sdwa %1, sext(%4) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1\n\t"
+      "v_cvt_f32_i32_sdwa %2, sext(%4) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+      "v_cvt_f32_i32_sdwa %3, sext(%4) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3\n\t"
+      "s_nop 1"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(w));
+}
+
+template <int ACT>
+__global__ __launch_bounds__(kLanesWaves * 64) void route_logits_lanes_kernel(
+    const void* __restrict__ x, int T, int H, const void* __restrict__ codes, const void* __restrict__ scales,
+    int E, int groups, int S, float* __restrict__ zp) {
+  __shared__ __align__(16) float4 xs[2][kChunkBlocks * 8 * 64];   // [buf][chunk slot * 64 + token]
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int g = blockIdx.y * kLanesWaves + __builtin_amdgcn_readfirstlane(tid / kWave);
+  const bool active = g < groups;
+  const int t0 = blockIdx.x * 64;
+  const int nb = H / 32, nu = nb / 2;
+  const int nbr = nb / S, b_beg = blockIdx.z * nbr;
+  const int n_chunks = nbr / kChunkBlocks;
+  // lane 16 r + n loads codes 4 n .. 4 n + 3 of a unit's 64 steps (block 2u: n < 8, then 2u + 1)
+  const int n = lane & 15;
+  const int woff = (n < 8 ? 0 : 8) + 16 * ((n & 7) >> 1) + 4 * (n & 1);
+  const uint8_t* cbase[kLaneGroup];
+  const uint8_t* sbase[kLaneGroup];
+#pragma unroll
+  for (int j = 0; j < kLaneGroup; ++j) {
+    const int e = min(g * kLaneGroup + j, E - 1);   // rows past E: a valid row, never stored
+    cbase[j] = reinterpret_cast<const uint8_t*>(codes) + code_off(e, 0, nu) + woff;
+    sbase[j] = reinterpret_cast<const uint8_t*>(scales) + Codes<FMT_Q8_0>::d_off(e, 0, nu);
+  }
+  uint32_t wr[kLaneGroup], dr[kLaneGroup];
+  auto load_unit = [&](int u) {
+#pragma unroll
+    for (int j = 0; j < kLaneGroup; ++j) {
+      wr[j] = *reinterpret_cast<const uint32_t*>(cbase[j] + (int64_t)u * 1024);
+      dr[j] = *reinterpret_cast<const uint32_t*>(sbase[j] + (int64_t)u * Codes<FMT_Q8_0>::kScaleUnit);
+    }
+  };
+
+  // staging of chunk c (4 blocks = 128 values of 64 tokens): thread tid moves the 4 values q =
+  // tid + 256 i; they are held as loaded (fp32, or bf16 bits) until stored, so that the wait for
+  // them falls after the chunk's arithmetic
+  using Raw = typename std::conditional<ACT == ACT_F32, float4, uint2>::type;
+  Raw stg[8];
+  auto fetch = [&](int c) {
+    const int h0 = 32 * (b_beg + kChunkBlocks * c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + 256 * i, tl = q / 32, cp = q % 32;
+      // every load is issued (tokens past T read the last token; their lanes store nothing), so
+      // that none sits behind a branch that would wait for it on the spot
+      const int64_t t = min(t0 + tl, T - 1);
+      stg[i] = *reinterpret_cast<const Raw*>(reinterpret_cast<const uint8_t*>(x) +
+                                             (t * H + h0 + 4 * cp) * (ACT == ACT_F32 ? 4 : 2));
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + 256 * i, tl = q / 32, cp = q % 32;
+      float4 v;
+      if constexpr (ACT == ACT_F32) {
+        v = stg[i];
+      } else {
+        v = make_float4(__uint_as_float(stg[i].x << 16), __uint_as_float(stg[i].x & 0xFFFF0000u),
+                        __uint_as_float(stg[i].y << 16), __uint_as_float(stg[i].y & 0xFFFF0000u));
+      }
+      xs[buf][cp * 64 + (tl ^ (cp & 15))] = v;
+    }
+  };
+
+  float lv[kMaxChunkLevels + 1][kLaneGroup];   // binary counter over the chunks
+#pragma unroll
+  for (int l = 0; l <= kMaxChunkLevels; ++l)
+#pragma unroll
+    for (int j = 0; j < kLaneGroup; ++j) lv[l][j] = 0.0f;
+  if (n_chunks > 0) {
+    fetch(0);
+    store(0);
+    load_unit(b_beg / 2);
+  }
+  for (int c = 0; c < n_chunks; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < n_chunks) fetch(c + 1);
+    __syncthreads();   // chunk c is in xs[buf]; nobody reads xs[buf ^ 1] any more
+    float v[kLaneGroup];
+    // the chunk's two units, their two blocks, their 32 steps: all unrolled at compile time, as
+    // the broadcast lane of a step is an immediate of its instruction
+    static_for<0, 2>([&](auto uu_) {
+      constexpr int uu = decltype(uu_)::value;
+      // the unit's weights (register k: steps 4 n + k) and its two block scales
+      float W[kLaneGroup][4], d[kLaneGroup][2];
+#pragma unroll
+      for (int j = 0; j < kLaneGroup; ++j) {
+        convert_codes(wr[j], W[j]);
+        d[j][0] = half_bits_to_float(dr[j] & 0xFFFFu);
+        d[j][1] = half_bits_to_float(dr[j] >> 16);
+      }
+      // next unit's codes and scales (the chunk's second unit, or the next chunk's first)
+      if (uu == 0 || c + 1 < n_chunks) load_unit(b_beg / 2 + 2 * c + uu + 1);
+      float half_sum[kLaneGroup];
+      static_for<0, 2>([&](auto hb_) {
+        constexpr int hb = decltype(hb_)::value;
+        float p[kLaneGroup];
+#pragma unroll
+        for (int j = 0; j < kLaneGroup; ++j) p[j] = 0.0f;
+        static_for<0, 8>([&](auto i4_) {
+          constexpr int i4 = decltype(i4_)::value;
+          constexpr int cp = 16 * uu + 8 * hb + i4;   // chunk slot: values 4 cp .. 4 cp + 3
+          const float4 xv = xs[buf][cp * 64 + (lane ^ (cp & 15))];
+          const float xq[4] = {xv.x, xv.y, xv.z, xv.w};
+          // step 32 hb + 4 i4 + k of the unit: weight register k, broadcast lane 8 hb + i4
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int j = 0; j < kLaneGroup; ++j) fmac_bcast<8 * hb + i4>(p[j], W[j][k], xq[k]);
+        });
+        // r_b = d_b * p_b, then the chunk's blocks pairwise: ((b0 + b1) + (b2 + b3))
+#pragma unroll
+        for (int j = 0; j < kLaneGroup; ++j) {
+          const float r = d[j][hb] * p[j];
+          half_sum[j] = hb == 0 ? r : half_sum[j] + r;
+        }
+      });
+#pragma unroll
+      for (int j = 0; j < kLaneGroup; ++j) v[j] = uu == 0 ? half_sum[j] : v[j] + half_sum[j];
+    });
+    if (active) {
+      bool placed = false;
+#pragma unroll
+      for (int l = 0; l < kMaxChunkLevels; ++l) {
+        if (!placed) {
+          if (!((c >> l) & 1)) {
+#pragma unroll
+            for (int j = 0; j < kLaneGroup; ++j) lv[l][j] = v[j];
+            placed = true;
+          } else {
+#pragma unroll
+            for (int j = 0; j < kLaneGroup; ++j) v[j] = lv[l][j] + v[j];
+          }
+        }
+      }
+      if (!placed) {
+#pragma unroll
+        for (int j = 0; j < kLaneGroup; ++j) lv[kMaxChunkLevels][j] = v[j];
+      }
+    }
+    if (c + 1 < n_chunks) store(buf ^ 1);
+  }
+  // n_chunks = 2^L: the range's sum is the subtree at level L
+  const int t = t0 + lane;
+  if (active && t < T && n_chunks > 0) {
+    const int L = 31 - __builtin_clz(n_chunks);
+    float r[kLaneGroup];
+#pragma unroll
+    for (int j = 0; j < kLaneGroup; ++j) r[j] = lv[0][j];
+#pragma unroll
+    for (int l = 1; l <= kMaxChunkLevels; ++l)
+      if (L == l) {
+#pragma unroll
+        for (int j = 0; j < kLaneGroup; ++j) r[j] = lv[l][j];
+      }
+    float* dst = zp + ((int64_t)blockIdx.z * T + t) * E + g * kLaneGroup;
+#pragma unroll
+    for (int j = 0; j < kLaneGroup; ++j)
+      if (g * kLaneGroup + j < E) dst[j] = r[j];
   }
 }
 
@@ -158,8 +419,27 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
 // untaken experts followed by a wave min of the expert index among those that
 // hold it (ties go to the lower index).  Weights: s_j = sigmoid(z_j) in fp64
 // on lane j, their sum taken in slot order by every lane, w_j = s_j / sum.
+// With S > 0 the logits arrive as S partial sums per (token, expert) (block ranges, zp[s][t][e]),
+// added here pairwise, level by level, and then the bias is added; with S == 0, z holds finished
+// logits.
 template <int EPL>  // experts per lane (E <= 64 * EPL)
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ z, int T, int E, int k,
+__device__ __forceinline__ float logit_of(const float* __restrict__ z, int S, const float* __restrict__ bias,
+                                          int T, int E, int t, int e) {
+  if (S == 0) return z[(int64_t)t * E + e];
+  float v[kMaxRanges];
+#pragma unroll
+  for (int i = 0; i < kMaxRanges; ++i) v[i] = i < S ? z[((int64_t)i * T + t) * E + e] : 0.0f;
+#pragma unroll
+  for (int w = 1; w < kMaxRanges; w <<= 1)
+#pragma unroll
+    for (int i = 0; i + w < kMaxRanges; i += 2 * w)
+      if (i + w < S) v[i] = v[i] + v[i + w];
+  return bias ? v[0] + bias[e] : v[0];
+}
+
+template <int EPL>  // experts per lane (E <= 64 * EPL)
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ z, int S,
+                                                         const float* __restrict__ bias, int T, int E, int k,
                                                          int32_t* __restrict__ ids, float* __restrict__ w) {
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
@@ -170,7 +450,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   for (int i = 0; i < EPL; ++i) {
     const int e = i * kWave + lane;
     live[i] = e < E;
-    key[i] = live[i] ? float_key(z[(int64_t)t * E + e]) : 0u;
+    key[i] = live[i] ? float_key(logit_of<EPL>(z, S, bias, T, E, t, e)) : 0u;
   }
   int my_id = -1;
   uint32_t my_key = 0;
@@ -224,30 +504,45 @@ static hipError_t launch_logits_c(int C, const void* x, int T, int H, const QMat
 }
 
 hipError_t launch_route(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
-                        int k, int32_t* ids, float* w, float* z_ws, hipStream_t s) {
-  const int nb = H / 32;
-  int C = 1;
-  while (C * kWave < nb) C <<= 1;
-  hipError_t err;
-  const bool q8 = fmt == FMT_Q8_0;
-  trace_pre("route_logits", s);
-  if (act == ACT_F32) {
-    err = q8 ? launch_logits_c<FMT_Q8_0, ACT_F32>(C, x, T, H, router, bias, z_ws, s)
-             : launch_logits_c<FMT_F32, ACT_F32>(C, x, T, H, router, bias, z_ws, s);
-  } else {
-    err = q8 ? launch_logits_c<FMT_Q8_0, ACT_BF16>(C, x, T, H, router, bias, z_ws, s)
-             : launch_logits_c<FMT_F32, ACT_BF16>(C, x, T, H, router, bias, z_ws, s);
-  }
-  trace_post("route_logits", s);
-  if (err != hipSuccess) return err;
+                        int k, int32_t* ids, float* w, void* ws, hipStream_t s) {
   const int E = router.rows;
+  const bool q8 = fmt == FMT_Q8_0;
+  hipError_t err = hipSuccess;
+  const LanesPlan lp = lanes_plan(T, E, H, fmt);
+  float* z = reinterpret_cast<float*>(ws);
+  int S = 0;
+  if (lp.use) {
+    const dim3 grid((T + 63) / 64, (lp.groups + kLanesWaves - 1) / kLanesWaves, lp.S);
+    trace_pre("route_logits", s);
+    if (act == ACT_F32)
+      route_logits_lanes_kernel<ACT_F32><<<grid, kLanesWaves * 64, 0, s>>>(x, T, H, router.codes, router.scales, E, lp.groups, lp.S, z);
+    else
+      route_logits_lanes_kernel<ACT_BF16><<<grid, kLanesWaves * 64, 0, s>>>(x, T, H, router.codes, router.scales, E, lp.groups, lp.S, z);
+    trace_post("route_logits", s);
+    err = hipGetLastError();
+    S = lp.S;
+  } else {
+    const int nb = H / 32;
+    int C = 1;
+    while (C * kWave < nb) C <<= 1;
+    trace_pre("route_logits", s);
+    if (act == ACT_F32) {
+      err = q8 ? launch_logits_c<FMT_Q8_0, ACT_F32>(C, x, T, H, router, bias, z, s)
+               : launch_logits_c<FMT_F32, ACT_F32>(C, x, T, H, router, bias, z, s);
+    } else {
+      err = q8 ? launch_logits_c<FMT_Q8_0, ACT_BF16>(C, x, T, H, router, bias, z, s)
+               : launch_logits_c<FMT_F32, ACT_BF16>(C, x, T, H, router, bias, z, s);
+    }
+    trace_post("route_logits", s);
+  }
+  if (err != hipSuccess) return err;
   dim3 grid((T + 3) / 4);
   trace_pre("route_topk", s);
-  if (E <= 64) route_topk_kernel<1><<<grid, 256, 0, s>>>(z_ws, T, E, k, ids, w);
-  else if (E <= 128) route_topk_kernel<2><<<grid, 256, 0, s>>>(z_ws, T, E, k, ids, w);
-  else if (E <= 256) route_topk_kernel<4><<<grid, 256, 0, s>>>(z_ws, T, E, k, ids, w);
-  else if (E <= 512) route_topk_kernel<8><<<grid, 256, 0, s>>>(z_ws, T, E, k, ids, w);
-  else route_topk_kernel<16><<<grid, 256, 0, s>>>(z_ws, T, E, k, ids, w);
+  if (E <= 64) route_topk_kernel<1><<<grid, 256, 0, s>>>(z, S, bias, T, E, k, ids, w);
+  else if (E <= 128) route_topk_kernel<2><<<grid, 256, 0, s>>>(z, S, bias, T, E, k, ids, w);
+  else if (E <= 256) route_topk_kernel<4><<<grid, 256, 0, s>>>(z, S, bias, T, E, k, ids, w);
+  else if (E <= 512) route_topk_kernel<8><<<grid, 256, 0, s>>>(z, S, bias, T, E, k, ids, w);
+  else route_topk_kernel<16><<<grid, 256, 0, s>>>(z, S, bias, T, E, k, ids, w);
   trace_post("route_topk", s);
   return hipGetLastError();
 }

@@ -217,3 +217,17 @@ def test_bf16_forward_format_limits():
     f = moe.workspace_size(2048, 4096, 2048, 8, 256, 256, moe.ACT_F32)
     assert a[2] >= 2048 * 8 * 2048 * 4 + 2048 * 4096 * 2
     assert f[2] == a[2] + 2048 * 4096 * 2       # fp32 activations add the lo plane
+
+
+def test_build_scan_flags_dpp_operand_written_too_late():
+    """The library build rejects a DPP instruction whose operand a vector instruction wrote fewer
+    than two wait states before (s_nop N counts N + 1)."""
+    from quantized_moe_routed_amd.build import _dpp_hazards
+    bad = "v_cvt_f32_i32_e32 v5, v1\n\tv_fmac_f32_dpp v3, v5, v4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+    assert len(_dpp_hazards(bad)) == 1
+    one = "v_cvt_f32_i32_e32 v5, v1\n\ts_nop 0\n\tv_fmac_f32_dpp v3, v5, v4 row_newbcast:0\n"
+    assert len(_dpp_hazards(one)) == 1
+    ok = "v_cvt_f32_i32_e32 v5, v1\n\ts_nop 1\n\tv_fmac_f32_dpp v3, v5, v4 row_newbcast:0\n"
+    assert _dpp_hazards(ok) == []
+    other = "v_cvt_f32_i32_e32 v6, v1\n\tv_fmac_f32_dpp v3, v5, v4 row_newbcast:0\n"
+    assert _dpp_hazards(other) == []

@@ -209,6 +209,23 @@ def test_cfg4_prefill_full_size(torch):
         assert sha(g["ids"], g["w"], g["counts"], g["offsets"], g["slot_list"], g["y"], g["out"]) == h0, rep
 
 
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_router_token_tiles_ragged(torch, act):
+    """Batches of 64+ tokens take the token-tiled logits kernel (tiles of 4 tokens, a share of the
+    tiles per workgroup row): T=133 leaves a partial tile and an uneven last share."""
+    _say(f"router token tiles: T=133, H=4096, E=256, k=8, {act}")
+    from quantized_moe_routed_amd.layer import act_code
+    wl = synth.make(2 if act == "f32" else 4, T=133)
+    layer = make_layer(wl)
+    x = x_tensor(wl, torch)
+    b = layer.buffers(wl.T, act_code(x))
+    layer.route(x, b)
+    torch.cuda.synchronize()
+    ids, w, _ = oracle.route(wl.x, wl.cfg.router_fmt, wl.router[0], wl.bias, wl.k)
+    assert np.array_equal(b.ids.cpu().numpy(), ids), "expert ids differ"
+    assert_close(b.w.cpu().numpy(), w, "weights")
+
+
 def test_bf16_small_shapes_and_share(torch):
     _say("bf16 small shapes: H=128, I=192, E=8, k=3, T=23; then an owned share and its complement")
     import quantized_moe_routed_amd as moe
