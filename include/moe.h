@@ -182,6 +182,22 @@ moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, i
 moe_status moe_combine(const float* y_slot, const float* w, const int32_t* ids, const int32_t* g2l,
                        int32_t T, int32_t k, int32_t H, int32_t E, float* out, hipStream_t s);
 
+/* The whole layer in one call: moe_route, moe_group_tokens, moe_expert_forward
+ * and moe_combine in turn on stream s, with their arguments and outputs (ids,
+ * w, counts, offsets, slot_list, y_slot, out) and the same results bit for bit;
+ * router->rows must equal E.  For batches of up to 8 tokens, the top-k
+ * selection, the grouping, the tile lists and the activation operands are
+ * produced by a single launch after the logits.
+ *   ws : route_ws + forward_ws bytes from moe_workspace_size, the router's part
+ *        first (route_ws is a multiple of 256), 16-byte aligned.
+ * All arguments are checked before the first launch; errors as for the four
+ * calls. */
+moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, int32_t I, int32_t k,
+                             const moe_qmat* router, const float* bias, const moe_experts* local,
+                             const int32_t* g2l, int32_t E, int32_t E_local, int32_t* ids, float* w,
+                             int32_t* counts, int32_t* offsets, int32_t* slot_list, float* y_slot,
+                             float* out, void* ws, size_t ws_bytes, hipStream_t s);
+
 /* ---- profiling ------------------------------------------------------------ */
 
 /* Record HIP events around launches of one kernel, for live per-kernel timing.

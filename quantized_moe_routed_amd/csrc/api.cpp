@@ -221,26 +221,36 @@ moe_status moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t k, int32_
   return ok();
 }
 
-moe_status moe_route(const void* x, int32_t xt, int32_t T, int32_t H, const moe_qmat* router, const float* bias,
-                     int32_t k, int32_t* ids, float* w, void* ws, size_t ws_bytes, hipStream_t s) {
-  if (T < 0) return fail(MOE_ERR_ARG, "moe_route: T < 0");
-  if (xt != MOE_ACT_F32 && xt != MOE_ACT_BF16) return fail(MOE_ERR_ARG, "moe_route: unknown activation type %d", xt);
-  if (!router) return fail(MOE_ERR_ARG, "moe_route: router is NULL");
-  if (H <= 0 || H % 32) return fail(MOE_ERR_ARG, "moe_route: H = %d is not a positive multiple of 32", H);
-  if (H > kMaxRouteH) return fail(MOE_ERR_UNSUPPORTED, "moe_route: H = %d exceeds %d", H, kMaxRouteH);
+}  // extern "C"
+
+namespace {
+
+// ---- argument checks and launch setup (shared by the four calls and the whole-layer call) ----
+// Each returns MOE_OK when every argument is valid (and, for T > 0, every pointer is memory of
+// the stream's device); nothing is launched by them.
+
+moe_status route_check(const char* fn, const void* x, int32_t xt, int32_t T, int32_t H, const moe_qmat* router,
+                       const float* bias, int32_t k, const int32_t* ids, const float* w, const void* ws,
+                       size_t ws_bytes, hipStream_t s) {
+  if (T < 0) return fail(MOE_ERR_ARG, "%s: T < 0", fn);
+  if (xt != MOE_ACT_F32 && xt != MOE_ACT_BF16) return fail(MOE_ERR_ARG, "%s: unknown activation type %d", fn, xt);
+  if (!router) return fail(MOE_ERR_ARG, "%s: router is NULL", fn);
+  if (H <= 0 || H % 32) return fail(MOE_ERR_ARG, "%s: H = %d is not a positive multiple of 32", fn, H);
+  if (H > kMaxRouteH) return fail(MOE_ERR_UNSUPPORTED, "%s: H = %d exceeds %d", fn, H, kMaxRouteH);
   const int E = router->rows;
-  if (E < 1) return fail(MOE_ERR_ARG, "moe_route: router has %d rows", E);
-  if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "moe_route: E = %d exceeds %d", E, kMaxE);
+  if (E < 1) return fail(MOE_ERR_ARG, "%s: router has %d rows", fn, E);
+  if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "%s: E = %d exceeds %d", fn, E, kMaxE);
   moe_status st = check_qmat(*router, "router", E, H, false, true);
   if (st) return st;
-  if (k < 1 || k > E) return fail(MOE_ERR_ARG, "moe_route: k = %d outside 1..E (E = %d)", k, E);
-  if (k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "moe_route: k = %d exceeds %d", k, kMaxK);
-  if (T > 0 && (!x || !ids || !w)) return fail(MOE_ERR_ARG, "moe_route: x, ids and w must not be NULL");
-  if (!aligned16(x)) return fail(MOE_ERR_ARG, "moe_route: x must be 16-byte aligned");
+  if (k < 1 || k > E) return fail(MOE_ERR_ARG, "%s: k = %d outside 1..E (E = %d)", fn, k, E);
+  if (k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "%s: k = %d exceeds %d", fn, k, kMaxK);
+  if (T > 0 && (!x || !ids || !w)) return fail(MOE_ERR_ARG, "%s: x, ids and w must not be NULL", fn);
+  if (!aligned16(x)) return fail(MOE_ERR_ARG, "%s: x must be 16-byte aligned", fn);
   const size_t need = route_ws_bytes(T, E, H, router->fmt);
   if (ws_bytes < need || (need && !ws))
-    return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu bytes, need %zu", ws_bytes, need);
-  if (T == 0) return ok();
+    return fail(MOE_ERR_WORKSPACE, "%s: router workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  if (!aligned16(ws)) return fail(MOE_ERR_ARG, "%s: workspace must be 16-byte aligned", fn);
+  if (T == 0) return MOE_OK;
   DevCheck dc;
   if ((st = stream_device(s, &dc.dev))) return st;
   dc(x, "x");
@@ -250,23 +260,16 @@ moe_status moe_route(const void* x, int32_t xt, int32_t T, int32_t H, const moe_
   dc(ids, "ids");
   dc(w, "w");
   dc(ws, "workspace");
-  if (dc.st) return dc.st;
-  if (!aligned16(ws)) return fail(MOE_ERR_ARG, "moe_route: workspace must be 16-byte aligned");
-  hipError_t e = moe::launch_route(x, xt, T, H, router->fmt, qm(*router), bias, k, ids, w, ws, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_route launch");
-  return ok();
+  return dc.st;
 }
 
-moe_status moe_group_tokens(const int32_t* ids, int32_t T, int32_t k, int32_t E, int32_t* counts, int32_t* offsets,
-                            int32_t* slot_list, void* ws, size_t ws_bytes, hipStream_t s) {
-  (void)ws;
-  (void)ws_bytes;
-  if (T < 0 || k < 1) return fail(MOE_ERR_ARG, "moe_group_tokens: T = %d, k = %d", T, k);
-  if (E < 1) return fail(MOE_ERR_ARG, "moe_group_tokens: E = %d", E);
-  if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "moe_group_tokens: E = %d exceeds %d", E, kMaxE);
-  if ((int64_t)T * k > (int64_t)0x7FFFFFFF) return fail(MOE_ERR_ARG, "moe_group_tokens: T*k overflows int32");
-  if (!counts || !offsets || (T > 0 && (!ids || !slot_list)))
-    return fail(MOE_ERR_ARG, "moe_group_tokens: NULL output or ids");
+moe_status group_check(const char* fn, const int32_t* ids, int32_t T, int32_t k, int32_t E, const int32_t* counts,
+                       const int32_t* offsets, const int32_t* slot_list, hipStream_t s) {
+  if (T < 0 || k < 1) return fail(MOE_ERR_ARG, "%s: T = %d, k = %d", fn, T, k);
+  if (E < 1) return fail(MOE_ERR_ARG, "%s: E = %d", fn, E);
+  if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "%s: E = %d exceeds %d", fn, E, kMaxE);
+  if ((int64_t)T * k > (int64_t)0x7FFFFFFF) return fail(MOE_ERR_ARG, "%s: T*k overflows int32", fn);
+  if (!counts || !offsets || (T > 0 && (!ids || !slot_list))) return fail(MOE_ERR_ARG, "%s: NULL output or ids", fn);
   moe_status st;
   DevCheck dc;
   if ((st = stream_device(s, &dc.dev))) return st;
@@ -279,47 +282,49 @@ moe_status moe_group_tokens(const int32_t* ids, int32_t T, int32_t k, int32_t E,
   if (lds > 64 * 1024) {
     // more than the default dynamic LDS for large expert counts (set per call: cheap, per device)
     hipError_t e = moe::group_set_lds_limit(lds);
-    if (e != hipSuccess) return hip_fail(e, "moe_group_tokens: LDS attribute");
+    if (e != hipSuccess) return hip_fail(e, "group LDS attribute");
   }
-  hipError_t e = moe::launch_group(ids, T, k, E, counts, offsets, slot_list, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_group_tokens launch");
-  return ok();
+  return MOE_OK;
 }
 
-moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, int32_t I, int32_t k,
-                              const moe_experts* local, const int32_t* g2l, int32_t E, int32_t E_local,
-                              const int32_t* counts, const int32_t* offsets, const int32_t* slot_list, float* y_slot,
-                              void* ws, size_t ws_bytes, hipStream_t s) {
-  if (T < 0) return fail(MOE_ERR_ARG, "moe_expert_forward: T < 0");
-  if (xt != MOE_ACT_F32 && xt != MOE_ACT_BF16)
-    return fail(MOE_ERR_ARG, "moe_expert_forward: unknown activation type %d", xt);
+// Checks of moe_expert_forward's arguments and the launch arguments (FFN launches and tile lists)
+// over the workspace.
+struct FwdSetup {
+  moe::FfnArgs a;
+  moe::TileLists tl;
+  FwdLayout L;
+};
+
+moe_status forward_setup(const char* fn, const void* x, int32_t xt, int32_t T, int32_t H, int32_t I, int32_t k,
+                         const moe_experts* local, const int32_t* g2l, int32_t E, int32_t E_local,
+                         const int32_t* counts, const int32_t* offsets, const int32_t* slot_list, float* y_slot,
+                         void* ws, size_t ws_bytes, hipStream_t s, FwdSetup& f) {
+  if (T < 0) return fail(MOE_ERR_ARG, "%s: T < 0", fn);
+  if (xt != MOE_ACT_F32 && xt != MOE_ACT_BF16) return fail(MOE_ERR_ARG, "%s: unknown activation type %d", fn, xt);
   if (H <= 0 || H % 32 || I <= 0 || I % 32)
-    return fail(MOE_ERR_ARG, "moe_expert_forward: H = %d, I = %d must be positive multiples of 32", H, I);
-  if (H > kMaxFfnDim || I > kMaxFfnDim)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_forward: H and I are limited to %d", kMaxFfnDim);
-  if (k < 1 || k > kMaxK) return fail(MOE_ERR_ARG, "moe_expert_forward: k = %d", k);
-  if (E < 1 || k > E) return fail(MOE_ERR_ARG, "moe_expert_forward: E = %d, k = %d", E, k);
-  if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "moe_expert_forward: E = %d exceeds %d", E, kMaxE);
-  if (!local) return fail(MOE_ERR_ARG, "moe_expert_forward: local experts is NULL");
+    return fail(MOE_ERR_ARG, "%s: H = %d, I = %d must be positive multiples of 32", fn, H, I);
+  if (H > kMaxFfnDim || I > kMaxFfnDim) return fail(MOE_ERR_UNSUPPORTED, "%s: H and I are limited to %d", fn, kMaxFfnDim);
+  if (k < 1 || k > kMaxK) return fail(MOE_ERR_ARG, "%s: k = %d", fn, k);
+  if (E < 1 || k > E) return fail(MOE_ERR_ARG, "%s: E = %d, k = %d", fn, E, k);
+  if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "%s: E = %d exceeds %d", fn, E, kMaxE);
+  if (!local) return fail(MOE_ERR_ARG, "%s: local experts is NULL", fn);
   if (local->n_experts != E_local || E_local < 1 || E_local > E)
-    return fail(MOE_ERR_ARG, "moe_expert_forward: E_local = %d but the owned stack holds %d experts (E = %d)",
-                E_local, local->n_experts, E);
-  if (!g2l && E_local != E)
-    return fail(MOE_ERR_ARG, "moe_expert_forward: no g2l table but only %d of %d experts owned", E_local, E);
+    return fail(MOE_ERR_ARG, "%s: E_local = %d but the owned stack holds %d experts (E = %d)", fn, E_local,
+                local->n_experts, E);
+  if (!g2l && E_local != E) return fail(MOE_ERR_ARG, "%s: no g2l table but only %d of %d experts owned", fn, E_local, E);
   moe_status st;
   if ((st = check_qmat(local->gate, "gate", I, H, true, false))) return st;
   if ((st = check_qmat(local->up, "up", I, H, true, false))) return st;
   if ((st = check_qmat(local->down, "down", H, I, true, false))) return st;
-  if (local->gate.fmt != local->up.fmt)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_forward: gate and up must share a format");
+  if (local->gate.fmt != local->up.fmt) return fail(MOE_ERR_UNSUPPORTED, "%s: gate and up must share a format", fn);
   if (T > 0 && (!x || !counts || !offsets || !slot_list || !y_slot))
-    return fail(MOE_ERR_ARG, "moe_expert_forward: NULL x, counts, offsets, slot_list or y_slot");
-  if (!aligned16(x) || !aligned16(y_slot))
-    return fail(MOE_ERR_ARG, "moe_expert_forward: x and y_slot must be 16-byte aligned");
-  const FwdLayout L = fwd_layout(T, H, I, k, E_local, xt);
+    return fail(MOE_ERR_ARG, "%s: NULL x, counts, offsets, slot_list or y_slot", fn);
+  if (!aligned16(x) || !aligned16(y_slot)) return fail(MOE_ERR_ARG, "%s: x and y_slot must be 16-byte aligned", fn);
+  f.L = fwd_layout(T, H, I, k, E_local, xt);
+  const FwdLayout& L = f.L;
   if (ws_bytes < L.total || !ws)
-    return fail(MOE_ERR_WORKSPACE, "moe_expert_forward: workspace %zu bytes, need %zu", ws_bytes, L.total);
-  if (T == 0) return ok();
+    return fail(MOE_ERR_WORKSPACE, "%s: expert workspace %zu bytes, need %zu", fn, ws_bytes, L.total);
+  if (T == 0) return MOE_OK;
   DevCheck dc;
   if ((st = stream_device(s, &dc.dev))) return st;
   dc(x, "x");
@@ -339,7 +344,8 @@ moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, i
 
   char* wsb = reinterpret_cast<char*>(ws);
   auto at16 = [&](size_t o) { return reinterpret_cast<uint16_t*>(wsb + o); };
-  moe::FfnArgs a{};
+  moe::FfnArgs& a = f.a;
+  a = moe::FfnArgs{};
   const TilePlan tp = tile_plan(T, H, I, k, E_local);
   a.T = T; a.H = H; a.I = I; a.k = k;
   a.fg = local->gate.fmt;
@@ -367,7 +373,8 @@ moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, i
   a.hs_hi = at16(L.hs_hi);
   a.hs_lo = at16(L.hs_lo);
   a.y = y_slot;
-  moe::TileLists tl{};
+  moe::TileLists& tl = f.tl;
+  tl = moe::TileLists{};
   tl.counts = counts;
   tl.offsets = offsets;
   tl.g2l = g2l;
@@ -386,21 +393,16 @@ moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, i
   tl.large = reinterpret_cast<int4*>(wsb + L.large);
   tl.n_small = reinterpret_cast<int32_t*>(wsb + L.n_small);
   tl.n_large = reinterpret_cast<int32_t*>(wsb + L.n_large);
-  hipError_t e = moe::launch_prep(x, xt, a.fg, T, H, a.nb32H, at16(L.xq_hi), xt == MOE_ACT_F32 ? at16(L.xq_lo) : nullptr,
-                                  at16(L.sq_hi), at16(L.sq_lo), reinterpret_cast<float*>(wsb + L.sigma), tl, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: prep launch");
-  e = moe::launch_ffn(a, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: FFN launch");
-  return ok();
+  return MOE_OK;
 }
 
-moe_status moe_combine(const float* y_slot, const float* w, const int32_t* ids, const int32_t* g2l, int32_t T,
-                       int32_t k, int32_t H, int32_t E, float* out, hipStream_t s) {
-  if (T < 0 || k < 1 || E < 1) return fail(MOE_ERR_ARG, "moe_combine: T = %d, k = %d, E = %d", T, k, E);
-  if (H <= 0 || H % 4) return fail(MOE_ERR_ARG, "moe_combine: H = %d must be a positive multiple of 4", H);
-  if (T > 0 && (!y_slot || !w || !ids || !out)) return fail(MOE_ERR_ARG, "moe_combine: NULL pointer");
-  if (!aligned16(y_slot) || !aligned16(out)) return fail(MOE_ERR_ARG, "moe_combine: y_slot and out must be 16-byte aligned");
-  if (T == 0) return ok();
+moe_status combine_check(const char* fn, const float* y_slot, const float* w, const int32_t* ids, const int32_t* g2l,
+                         int32_t T, int32_t k, int32_t H, int32_t E, const float* out, hipStream_t s) {
+  if (T < 0 || k < 1 || E < 1) return fail(MOE_ERR_ARG, "%s: T = %d, k = %d, E = %d", fn, T, k, E);
+  if (H <= 0 || H % 4) return fail(MOE_ERR_ARG, "%s: H = %d must be a positive multiple of 4", fn, H);
+  if (T > 0 && (!y_slot || !w || !ids || !out)) return fail(MOE_ERR_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(y_slot) || !aligned16(out)) return fail(MOE_ERR_ARG, "%s: y_slot and out must be 16-byte aligned", fn);
+  if (T == 0) return MOE_OK;
   moe_status st;
   DevCheck dc;
   if ((st = stream_device(s, &dc.dev))) return st;
@@ -409,9 +411,117 @@ moe_status moe_combine(const float* y_slot, const float* w, const int32_t* ids, 
   dc(ids, "ids");
   dc(g2l, "g2l");
   dc(out, "out");
-  if (dc.st) return dc.st;
+  return dc.st;
+}
+
+hipError_t launch_prep_of(const FwdSetup& f, const void* x, int xt, hipStream_t s) {
+  return moe::launch_prep(x, xt, f.a.fg, f.a.T, f.a.H, f.a.nb32H, const_cast<uint16_t*>(f.a.xq_hi),
+                          const_cast<uint16_t*>(f.a.xq_lo), const_cast<uint16_t*>(f.a.sq_hi),
+                          const_cast<uint16_t*>(f.a.sq_lo), const_cast<float*>(f.a.sigma), f.tl, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_route(const void* x, int32_t xt, int32_t T, int32_t H, const moe_qmat* router, const float* bias,
+                     int32_t k, int32_t* ids, float* w, void* ws, size_t ws_bytes, hipStream_t s) {
+  moe_status st = route_check("moe_route", x, xt, T, H, router, bias, k, ids, w, ws, ws_bytes, s);
+  if (st) return st;
+  if (T == 0) return ok();
+  hipError_t e = moe::launch_route(x, xt, T, H, router->fmt, qm(*router), bias, k, ids, w, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_route launch");
+  return ok();
+}
+
+moe_status moe_group_tokens(const int32_t* ids, int32_t T, int32_t k, int32_t E, int32_t* counts, int32_t* offsets,
+                            int32_t* slot_list, void* ws, size_t ws_bytes, hipStream_t s) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status st = group_check("moe_group_tokens", ids, T, k, E, counts, offsets, slot_list, s);
+  if (st) return st;
+  hipError_t e = moe::launch_group(ids, T, k, E, counts, offsets, slot_list, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_group_tokens launch");
+  return ok();
+}
+
+moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, int32_t I, int32_t k,
+                              const moe_experts* local, const int32_t* g2l, int32_t E, int32_t E_local,
+                              const int32_t* counts, const int32_t* offsets, const int32_t* slot_list, float* y_slot,
+                              void* ws, size_t ws_bytes, hipStream_t s) {
+  FwdSetup f;
+  moe_status st = forward_setup("moe_expert_forward", x, xt, T, H, I, k, local, g2l, E, E_local, counts, offsets,
+                                slot_list, y_slot, ws, ws_bytes, s, f);
+  if (st) return st;
+  if (T == 0) return ok();
+  hipError_t e = launch_prep_of(f, x, xt, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: prep launch");
+  e = moe::launch_ffn(f.a, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_expert_forward: FFN launch");
+  return ok();
+}
+
+moe_status moe_combine(const float* y_slot, const float* w, const int32_t* ids, const int32_t* g2l, int32_t T,
+                       int32_t k, int32_t H, int32_t E, float* out, hipStream_t s) {
+  moe_status st = combine_check("moe_combine", y_slot, w, ids, g2l, T, k, H, E, out, s);
+  if (st) return st;
+  if (T == 0) return ok();
   hipError_t e = moe::launch_combine(y_slot, w, ids, g2l, T, k, H, E, out, s);
   if (e != hipSuccess) return hip_fail(e, "moe_combine launch");
+  return ok();
+}
+
+moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, int32_t I, int32_t k,
+                             const moe_qmat* router, const float* bias, const moe_experts* local, const int32_t* g2l,
+                             int32_t E, int32_t E_local, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                             int32_t* slot_list, float* y_slot, float* out, void* ws, size_t ws_bytes, hipStream_t s) {
+  const char* fn = "moe_layer_forward";
+  if (!router) return fail(MOE_ERR_ARG, "%s: router is NULL", fn);
+  if (router->rows != E) return fail(MOE_ERR_ARG, "%s: router has %d rows but E = %d", fn, router->rows, E);
+  if (H <= 0 || H % 32 || E < 1 || E > kMaxE) return fail(MOE_ERR_ARG, "%s: H = %d, E = %d", fn, H, E);
+  if (T < 0) return fail(MOE_ERR_ARG, "%s: T < 0", fn);
+  // the router's part of the workspace first, then the expert part
+  const size_t rws = route_ws_bytes(T, E, H);
+  if (ws_bytes < rws) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need more than %zu", fn, ws_bytes, rws);
+  char* wsb = reinterpret_cast<char*>(ws);
+  moe_status st = route_check(fn, x, xt, T, H, router, bias, k, ids, w, ws, rws, s);
+  if (st) return st;
+  if ((st = group_check(fn, ids, T, k, E, counts, offsets, slot_list, s))) return st;
+  FwdSetup f;
+  if ((st = forward_setup(fn, x, xt, T, H, I, k, local, g2l, E, E_local, counts, offsets, slot_list, y_slot,
+                          wsb ? wsb + rws : nullptr, ws_bytes - rws, s, f)))
+    return st;
+  if ((st = combine_check(fn, y_slot, w, ids, g2l, T, k, H, E, out, s))) return st;
+  hipError_t e;
+  if (T == 0) {
+    // as the four calls: only the grouping writes anything (zero counts and offsets)
+    e = moe::launch_group(ids, T, k, E, counts, offsets, slot_list, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: group launch");
+    return ok();
+  }
+  if (T <= moe::kFrontMaxTokens) {
+    const size_t lds = moe::front_lds_bytes(T, E, k);
+    if (lds > 160 * 1024) return fail(MOE_ERR_UNSUPPORTED, "%s: E = %d needs %zu bytes of LDS", fn, E, lds);
+    int S = 0;
+    e = moe::launch_logits(x, xt, T, H, router->fmt, qm(*router), bias, ws, &S, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: logits launch");
+    e = moe::launch_front(reinterpret_cast<const float*>(ws), S, bias, T, E, k, ids, w, counts, offsets, slot_list, x,
+                          xt, H, f.a.nb32H, const_cast<uint16_t*>(f.a.xq_hi), const_cast<uint16_t*>(f.a.xq_lo),
+                          const_cast<uint16_t*>(f.a.sq_hi), const_cast<uint16_t*>(f.a.sq_lo),
+                          const_cast<float*>(f.a.sigma), f.tl, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: selection launch");
+  } else {
+    e = moe::launch_route(x, xt, T, H, router->fmt, qm(*router), bias, k, ids, w, ws, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: route launch");
+    e = moe::launch_group(ids, T, k, E, counts, offsets, slot_list, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: group launch");
+    e = launch_prep_of(f, x, xt, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: prep launch");
+  }
+  e = moe::launch_ffn(f.a, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: FFN launch");
+  e = moe::launch_combine(y_slot, w, ids, g2l, T, k, H, E, out, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: combine launch");
   return ok();
 }
 

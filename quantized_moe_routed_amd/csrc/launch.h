@@ -16,6 +16,10 @@ void trace_post(const char* name, hipStream_t s);
 hipError_t launch_route(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
                         int k, int32_t* ids, float* w, void* ws, hipStream_t s);
 size_t route_ws_need(int T, int E, int H, int fmt);   // workspace bytes of launch_route
+// The logits alone, into ws: finished logits (*S = 0) or S partial sums per (token, expert) whose
+// pairwise sum plus the bias is the logit (*S > 0); the selection kernels take either.
+hipError_t launch_logits(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
+                         void* ws, int* S, hipStream_t s);
 
 hipError_t launch_group(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
                         int32_t* slot_list, hipStream_t s);
@@ -35,6 +39,15 @@ struct TileLists {
   const int32_t* slot_list;
   int k;
 };
+
+// Batches of up to kFrontMaxTokens tokens: top-k selection, grouping, tile lists and the
+// activation operands in one launch (prep.hip), after launch_logits.
+constexpr int kFrontMaxTokens = 8;
+size_t front_lds_bytes(int T, int E, int k);
+hipError_t launch_front(const float* z, int S, const float* bias, int T, int E, int k, int32_t* ids, float* w,
+                        int32_t* counts, int32_t* offsets, int32_t* slot_list, const void* x, int act, int H,
+                        int nb32, uint16_t* xq_hi, uint16_t* xq_lo, uint16_t* sq_hi, uint16_t* sq_lo, float* sigma,
+                        const TileLists& tl, hipStream_t s);
 
 // Arguments of the expert FFN launches (workspace pointers included).
 struct FfnArgs {

@@ -12,6 +12,7 @@
 #include "device.h"
 #include "fmt.h"
 #include "launch.h"
+#include "select.h"
 
 namespace moe {
 
@@ -71,7 +72,7 @@ __device__ void build_tiles(const int32_t* __restrict__ counts, const int32_t* _
   }
 }
 
-template <int ACT, int FMT>
+template <int ACT>
 __device__ void prep_token(const void* __restrict__ x, int t, int H, int nb32, uint16_t* __restrict__ xq_hi,
                            uint16_t* __restrict__ xq_lo, uint16_t* __restrict__ sq_hi, uint16_t* __restrict__ sq_lo,
                            float* __restrict__ sigma) {
@@ -125,7 +126,7 @@ __device__ void prep_token(const void* __restrict__ x, int t, int H, int nb32, u
   }
 }
 
-template <int ACT, int FMT>
+template <int ACT>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const void* __restrict__ x, int T, int H, int nb32,
                                                             uint16_t* __restrict__ xq_hi, uint16_t* __restrict__ xq_lo,
                                                             uint16_t* __restrict__ sq_hi, uint16_t* __restrict__ sq_lo,
@@ -138,25 +139,125 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const void* __restri
                 tl.max_large, tl.large, tl.n_large, wave_tot);
   } else {
     const int t = blockIdx.x - 1;
-    if (t < T) prep_token<ACT, FMT>(x, t, H, nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma);
+    if (t < T) prep_token<ACT>(x, t, H, nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma);
   }
 }
 
 hipError_t launch_prep(const void* x, int act, int fmt, int T, int H, int nb32, uint16_t* xq_hi, uint16_t* xq_lo,
                        uint16_t* sq_hi, uint16_t* sq_lo, float* sigma, const TileLists& tl, hipStream_t s) {
+  (void)fmt;   // the operand layout is the same for both weight formats
   const dim3 grid(1 + T);
   trace_pre("prep", s);
-#define MOE_PREP(A, F) \
-  prep_kernel<A, F><<<grid, kPrepThreads, 0, s>>>(x, T, H, nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma, tl)
-  if (act == ACT_F32) {
-    if (fmt == FMT_Q2SM) MOE_PREP(ACT_F32, FMT_Q2SM);
-    else MOE_PREP(ACT_F32, FMT_Q8_0);
-  } else {
-    if (fmt == FMT_Q2SM) MOE_PREP(ACT_BF16, FMT_Q2SM);
-    else MOE_PREP(ACT_BF16, FMT_Q8_0);
-  }
-#undef MOE_PREP
+  if (act == ACT_F32)
+    prep_kernel<ACT_F32><<<grid, kPrepThreads, 0, s>>>(x, T, H, nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma, tl);
+  else
+    prep_kernel<ACT_BF16><<<grid, kPrepThreads, 0, s>>>(x, T, H, nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma, tl);
   trace_post("prep", s);
+  return hipGetLastError();
+}
+
+// ---- small batches: selection, grouping, tile lists and operands in one launch ----------------
+// Workgroup 0 takes the top-k of every token (wave w: tokens w, w + 16, ...), groups the slots by
+// expert (a direct stable counting sort of at most 8 k slots) and builds the tile lists, keeping
+// ids, counts, offsets and the slot list in LDS between the steps (each step reads what other
+// threads wrote); the other workgroups prepare one token's operand each, which does not depend on
+// the routing.
+template <int EPL, int ACT>
+__global__ __launch_bounds__(kPrepThreads) void front_kernel(const float* __restrict__ z, int S,
+                                                             const float* __restrict__ bias, int T, int E, int k,
+                                                             int32_t* __restrict__ ids,
+                                                             float* __restrict__ w, int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ slot_list, const void* __restrict__ x,
+                                                             int H, int nb32, uint16_t* __restrict__ xq_hi,
+                                                             uint16_t* __restrict__ xq_lo, uint16_t* __restrict__ sq_hi,
+                                                             uint16_t* __restrict__ sq_lo, float* __restrict__ sigma,
+                                                             TileLists tl) {
+  extern __shared__ int32_t fsm[];   // counts [E], offsets [E + 1], ids [T k], slots [T k]
+  __shared__ int32_t wave_tot[kPrepThreads / kWave];
+  if (blockIdx.x == 0) {
+    const int tid = threadIdx.x, wave = tid / kWave, n = T * k;
+    int32_t* s_cnt = fsm;
+    int32_t* s_off = s_cnt + E;
+    int32_t* s_ids = s_off + E + 1;
+    int32_t* s_slot = s_ids + n;
+    for (int t = wave; t < T; t += kPrepThreads / kWave) topk_token<EPL>(z, S, bias, T, E, k, t, ids, w, s_ids);
+    __syncthreads();
+    // the stable counting sort of a few slots, directly: expert e's count and offset are the slots
+    // with id e and with a smaller id; slot i goes to (slots with a smaller id) + (earlier slots
+    // with its id).  Ids outside [0, E) take part in nothing.
+    for (int e = tid; e < E; e += kPrepThreads) {
+      int c = 0, o = 0;
+      for (int i = 0; i < n; ++i) {
+        const int v = s_ids[i];
+        c += v == e;
+        o += (unsigned)v < (unsigned)e;
+      }
+      s_cnt[e] = c;
+      s_off[e] = o;
+    }
+    if (tid == 0) {
+      int c = 0;
+      for (int i = 0; i < n; ++i) c += (unsigned)s_ids[i] < (unsigned)E;
+      s_off[E] = c;
+    }
+    for (int i = tid; i < n; i += kPrepThreads) {
+      const int v = s_ids[i];
+      if ((unsigned)v < (unsigned)E) {
+        int r = 0;
+        for (int j = 0; j < n; ++j) {
+          const int u = s_ids[j];
+          r += (unsigned)u < (unsigned)v || (u == v && j < i);
+        }
+        s_slot[r] = i;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += kPrepThreads) slot_list[i] = s_slot[i];
+    for (int e = tid; e <= E; e += kPrepThreads) {
+      if (e < E) counts[e] = s_cnt[e];
+      offsets[e] = s_off[e];
+    }
+    build_tiles(s_cnt, s_off, tl.g2l, E, tl.E_local, tl.n_slots, tl.bm_small, 1, tl.large_min, tl.max_small,
+                tl.small, tl.n_small, wave_tot, tl.small_tok, s_slot, k);
+    build_tiles(s_cnt, s_off, tl.g2l, E, tl.E_local, tl.n_slots, tl.bm_large, tl.large_min, 0x7FFFFFFF, tl.max_large,
+                tl.large, tl.n_large, wave_tot);
+  } else {
+    const int t = blockIdx.x - 1;
+    if (t < T) prep_token<ACT>(x, t, H, nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma);
+  }
+}
+
+size_t front_lds_bytes(int T, int E, int k) { return sizeof(int32_t) * (2 * (size_t)E + 1 + 2 * (size_t)T * k); }
+
+hipError_t launch_front(const float* z, int S, const float* bias, int T, int E, int k, int32_t* ids, float* w,
+                        int32_t* counts, int32_t* offsets, int32_t* slot_list, const void* x, int act, int H,
+                        int nb32, uint16_t* xq_hi, uint16_t* xq_lo, uint16_t* sq_hi, uint16_t* sq_lo, float* sigma,
+                        const TileLists& tl, hipStream_t s) {
+  const size_t lds = front_lds_bytes(T, E, k);
+  const dim3 grid(1 + T);
+#define MOE_FRONT(EPL, A)                                                                                       \
+  do {                                                                                                          \
+    auto kern = front_kernel<EPL, A>;                                                                           \
+    if (lds > 64 * 1024) {                                                                                      \
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),                            \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);          \
+      if (e != hipSuccess) return e;                                                                            \
+    }                                                                                                           \
+    kern<<<grid, kPrepThreads, lds, s>>>(z, S, bias, T, E, k, ids, w, counts, offsets, slot_list, x, H,  \
+                                         nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma, tl);                          \
+  } while (0)
+#define MOE_FRONT_E(A)                  \
+  if (E <= 64) MOE_FRONT(1, A);         \
+  else if (E <= 128) MOE_FRONT(2, A);   \
+  else if (E <= 256) MOE_FRONT(4, A);   \
+  else if (E <= 512) MOE_FRONT(8, A);   \
+  else MOE_FRONT(16, A);
+  trace_pre("front", s);
+  if (act == ACT_F32) { MOE_FRONT_E(ACT_F32) } else { MOE_FRONT_E(ACT_BF16) }
+  trace_post("front", s);
+#undef MOE_FRONT_E
+#undef MOE_FRONT
   return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@
 #include "device.h"
 #include "fmt.h"
 #include "launch.h"
+#include "select.h"
 
 namespace moe {
 
@@ -178,7 +179,6 @@ constexpr int kLaneGroup = 8;          // experts per wave
 constexpr int kLanesWaves = 4;
 constexpr int kChunkBlocks = 4;
 constexpr int kMaxChunkLevels = 7;     // up to 128 chunks (512 blocks) per range
-constexpr int kMaxRanges = 32;         // block ranges S (a power of two)
 
 struct LanesPlan {
   bool use;
@@ -387,105 +387,12 @@ __global__ __launch_bounds__(kLanesWaves * 64) void route_logits_lanes_kernel(
   }
 }
 
-// Order-preserving unsigned key of a logit: larger z -> larger key, -0 and +0
-// equal, NaN -> 0 (below every number).  key_to_float inverts it (0 -> NaN).
-__device__ __forceinline__ uint32_t float_key(float z) {
-  if (z != z) return 0u;
-  if (z == 0.0f) z = 0.0f;   // -0 -> +0
-  const uint32_t b = __float_as_uint(z);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-__device__ __forceinline__ float key_to_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-// Wave-wide max / min of an unsigned value: quad and row permutes (DPP) reduce
-// each row of 16 lanes, then the four row results are read out.
-template <bool MAX>
-__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
-  auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
-  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-  return op(op(r0, r1), op(r2, r3));
-}
-
-// One wave per token: k rounds, each a wave max of the logit key over the
-// untaken experts followed by a wave min of the expert index among those that
-// hold it (ties go to the lower index).  Weights: s_j = sigmoid(z_j) in fp64
-// on lane j, their sum taken in slot order by every lane, w_j = s_j / sum.
-// With S > 0 the logits arrive as S partial sums per (token, expert) (block ranges, zp[s][t][e]),
-// added here pairwise, level by level, and then the bias is added; with S == 0, z holds finished
-// logits.
-template <int EPL>  // experts per lane (E <= 64 * EPL)
-__device__ __forceinline__ float logit_of(const float* __restrict__ z, int S, const float* __restrict__ bias,
-                                          int T, int E, int t, int e) {
-  if (S == 0) return z[(int64_t)t * E + e];
-  float v[kMaxRanges];
-#pragma unroll
-  for (int i = 0; i < kMaxRanges; ++i) v[i] = i < S ? z[((int64_t)i * T + t) * E + e] : 0.0f;
-#pragma unroll
-  for (int w = 1; w < kMaxRanges; w <<= 1)
-#pragma unroll
-    for (int i = 0; i + w < kMaxRanges; i += 2 * w)
-      if (i + w < S) v[i] = v[i] + v[i + w];
-  return bias ? v[0] + bias[e] : v[0];
-}
-
-template <int EPL>  // experts per lane (E <= 64 * EPL)
+template <int EPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ z, int S,
                                                          const float* __restrict__ bias, int T, int E, int k,
                                                          int32_t* __restrict__ ids, float* __restrict__ w) {
-  const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (t >= T) return;
-  uint32_t key[EPL];
-  bool live[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = i * kWave + lane;
-    live[i] = e < E;
-    key[i] = live[i] ? float_key(logit_of<EPL>(z, S, bias, T, E, t, e)) : 0u;
-  }
-  int my_id = -1;
-  uint32_t my_key = 0;
-  for (int j = 0; j < k; ++j) {
-    uint32_t lk = 0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (live[i] && key[i] > lk) lk = key[i];
-    const uint32_t mk = wave_reduce_u32<true>(lk);
-    uint32_t li = 0xFFFFFFFFu;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const uint32_t e = (uint32_t)(i * kWave + lane);
-      if (live[i] && key[i] == mk && e < li) li = e;
-    }
-    const uint32_t me = wave_reduce_u32<false>(li);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if ((uint32_t)(i * kWave + lane) == me) live[i] = false;
-    if (lane == j) {
-      my_id = (int)me;
-      my_key = mk;
-    }
-  }
-  const double my_s = 1.0 / (1.0 + exp(-(double)key_to_float(my_key)));
-  double ssum = 0.0;
-  for (int j = 0; j < k; ++j) {
-    const int lo = __builtin_amdgcn_readlane((int)(uint32_t)__double_as_longlong(my_s), j);
-    const int hi = __builtin_amdgcn_readlane((int)(uint32_t)(__double_as_longlong(my_s) >> 32), j);
-    ssum += __longlong_as_double(((long long)(uint32_t)hi << 32) | (uint32_t)lo);
-  }
-  if (lane < k) {
-    ids[(int64_t)t * k + lane] = my_id;
-    w[(int64_t)t * k + lane] = (float)(my_s / ssum);
-  }
+  if (t < T) topk_token<EPL>(z, S, bias, T, E, k, t, ids, w);
 }
 
 template <int FMT, int ACT>
@@ -503,8 +410,8 @@ static hipError_t launch_logits_c(int C, const void* x, int T, int H, const QMat
   return hipGetLastError();
 }
 
-hipError_t launch_route(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
-                        int k, int32_t* ids, float* w, void* ws, hipStream_t s) {
+hipError_t launch_logits(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
+                         void* ws, int* S_out, hipStream_t s) {
   const int E = router.rows;
   const bool q8 = fmt == FMT_Q8_0;
   hipError_t err = hipSuccess;
@@ -535,7 +442,17 @@ hipError_t launch_route(const void* x, int act, int T, int H, int fmt, const QMa
     }
     trace_post("route_logits", s);
   }
+  *S_out = S;
+  return err;
+}
+
+hipError_t launch_route(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
+                        int k, int32_t* ids, float* w, void* ws, hipStream_t s) {
+  const int E = router.rows;
+  int S = 0;
+  hipError_t err = launch_logits(x, act, T, H, fmt, router, bias, ws, &S, s);
   if (err != hipSuccess) return err;
+  const float* z = reinterpret_cast<const float*>(ws);
   dim3 grid((T + 3) / 4);
   trace_pre("route_topk", s);
   if (E <= 64) route_topk_kernel<1><<<grid, 256, 0, s>>>(z, S, bias, T, E, k, ids, w);

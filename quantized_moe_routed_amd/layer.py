@@ -14,7 +14,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (ACT_BF16, ACT_F32, W_F32, Experts, combine, expert_forward, group_tokens, pack_planar, plan_check,
+from . import (ACT_BF16, ACT_F32, W_F32, Experts, combine, expert_forward, group_tokens, layer_forward, pack_planar,
+               plan_check,
                qmat, route, workspace_size)
 
 
@@ -51,8 +52,9 @@ class Buffers:
     slot_list: torch.Tensor
     y_slot: torch.Tensor
     out: torch.Tensor
-    route_ws: torch.Tensor
+    route_ws: torch.Tensor          # views into ws: the router's part, then the experts' part
     fwd_ws: torch.Tensor
+    ws: torch.Tensor
 
 
 class MoELayer:
@@ -86,6 +88,7 @@ class MoELayer:
         d = self.device
         rws, _, fws = workspace_size(T, self.H, self.I, self.k, self.E, self.E_local, xt)
         i32 = dict(dtype=torch.int32, device=d)
+        ws = torch.empty(rws + max(fws, 1), dtype=torch.uint8, device=d)
         return Buffers(
             T=T, xt=xt,
             ids=torch.empty((T, self.k), **i32),
@@ -95,8 +98,9 @@ class MoELayer:
             slot_list=torch.empty(max(T * self.k, 1), **i32),
             y_slot=torch.zeros((T * self.k, self.H), dtype=torch.float32, device=d),
             out=torch.empty((T, self.H), dtype=torch.float32, device=d),
-            route_ws=torch.empty(max(rws, 1), dtype=torch.uint8, device=d),
-            fwd_ws=torch.empty(max(fws, 1), dtype=torch.uint8, device=d),
+            route_ws=ws[:rws] if rws else ws[:1],
+            fwd_ws=ws[rws:],
+            ws=ws,
         )
 
     # the four calls, each a thin wrapper
@@ -114,11 +118,19 @@ class MoELayer:
     def combine(self, b: Buffers, stream=None):
         combine(b.y_slot, b.w, b.ids, self.g2l, b.T, self.k, self.H, self.E, b.out, stream)
 
-    def run(self, x: torch.Tensor, b: Buffers, stream=None):
+    def run_calls(self, x: torch.Tensor, b: Buffers, stream=None):
+        """The layer as the four calls in turn."""
         self.route(x, b, stream)
         self.group(b, stream)
         self.forward(x, b, stream)
         self.combine(b, stream)
+        return b.out
+
+    def run(self, x: torch.Tensor, b: Buffers, stream=None):
+        """The layer as one call (moe_layer_forward): the four calls' results, fewer launches."""
+        layer_forward(x, b.xt, b.T, self.H, self.I, self.k, self._router_q, self.bias, self._experts, self.g2l,
+                      self.E, self.E_local, b.ids, b.w, b.counts, b.offsets, b.slot_list, b.y_slot, b.out, b.ws,
+                      b.ws.numel(), stream)
         return b.out
 
 

@@ -273,3 +273,39 @@ def test_large_tiles_against_oracle(torch, name):
     if name == "f32_multi_tile":
         assert counts.max() > 2 * 128
     check_against_oracle(wl, got, oracle_expect(wl), what=f"large {name}")
+
+
+def _run_both(layer, wl, torch):
+    from quantized_moe_routed_amd.layer import act_code
+    x = x_tensor(wl, torch)
+    outs = []
+    for fused in (False, True):
+        b = layer.buffers(wl.T, act_code(x))
+        (layer.run if fused else layer.run_calls)(x, b)
+        torch.cuda.synchronize()
+        outs.append([b.ids.cpu().numpy(), b.w.cpu().numpy(), b.counts.cpu().numpy(), b.offsets.cpu().numpy(),
+                     b.slot_list.cpu().numpy()[: wl.T * wl.k], b.y_slot.cpu().numpy(), b.out.cpu().numpy()])
+    return outs
+
+
+@pytest.mark.parametrize("cfg,T", [(2, 1), (2, 8), (3, 9), (3, 32), (4, 20)])
+def test_layer_call_equals_the_four_calls(torch, cfg, T):
+    """moe_layer_forward (one launch for selection, grouping, tiles and operands up to 8 tokens)
+    gives the four calls' results bit for bit, on both sides of the 8-token switch."""
+    _say(f"layer call vs four calls: cfg{cfg} T={T}")
+    wl = synth.make(cfg, T=T)
+    calls, fused = _run_both(make_layer(wl), wl, torch)
+    for name, a, b in zip(("ids", "w", "counts", "offsets", "slot_list", "y_slot", "out"), calls, fused):
+        assert np.array_equal(a, b), f"{name} differs between the layer call and the four calls"
+
+
+def test_layer_call_owned_share(torch):
+    """The layer call with an owned-expert table (a share of the experts): the four calls' partial."""
+    _say("layer call vs four calls: cfg5 share, T=24")
+    wl = synth.make(5, T=24)
+    import quantized_moe_routed_amd as moe
+    owner = moe.place_lpt(np.arange(wl.E, dtype=np.int64) % 7 + 1, 2)
+    g2l, l2g = moe.share_tables(owner, 0)
+    calls, fused = _run_both(make_layer(wl, l2g=l2g, g2l=g2l), wl, torch)
+    for name, a, b in zip(("ids", "w", "counts", "offsets", "slot_list", "y_slot", "out"), calls, fused):
+        assert np.array_equal(a, b), f"{name} differs between the layer call and the four calls"
