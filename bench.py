@@ -1,8 +1,9 @@
 """Benchmark of the routed-expert MoE layer on one MI355X.
 
-One step = one pass of the whole layer (moe_route, moe_group_tokens,
-moe_expert_forward, moe_combine) over one batch of synthetic input that is
-already resident in device memory.
+One step = one pass of the whole layer (moe_layer_forward: routing, grouping,
+the owned experts' FFN and the combine, with the results of the four calls
+moe_route, moe_group_tokens, moe_expert_forward, moe_combine) over one batch of
+synthetic input that is already resident in device memory.
 
 The headline workload is single-token decode (T=1, H=4096, 256 experts,
 I=2048, top-8, 2-bit gate/up/down, Q8_0 router, fp32 activations).  Every step
@@ -12,8 +13,9 @@ last-level cache, as real decode does.  The same JSON line also carries the
 other workloads (batched decode, prefill on bf16 matrix cores, one expert-
 parallel share) measured the same way, under "workloads".
 
-Kernel times come from HIP events that the library records around each launch
-of the named kernel during the timed region (on the stream the kernel runs on).
+Kernel times come from HIP events that the library records around every
+eighth launch of the named kernel during the timed region (on the stream the
+kernel runs on).
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -77,6 +79,7 @@ def input_pool(wl, n_batches, torch):
 
 
 LARGE_MIN = 16   # experts with this many slots or more run on the large-tile kernel (batches of 16+ tokens)
+TRACE_EVERY = 8  # the kernel events of the timed region sample one launch in this many
 
 
 def time_layer(layer, xs, steps, warmup, kernel, torch):
@@ -89,7 +92,9 @@ def time_layer(layer, xs, steps, warmup, kernel, torch):
     for i in range(warmup):
         layer.run(xs[i % len(xs)], b)
     torch.cuda.synchronize()
-    trace = moe.KernelTrace(kernel, steps)
+    # events around every TRACE_EVERY-th launch of the kernel only: each pair of events costs the
+    # stream a few microseconds, which would otherwise be charged to every step
+    trace = moe.KernelTrace(kernel, (steps + TRACE_EVERY - 1) // TRACE_EVERY, TRACE_EVERY)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

@@ -204,11 +204,17 @@ moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, in
  * While set (on the calling thread), the i-th launch of the kernel called
  * `name` gets hipEventRecord(start[i]) before and hipEventRecord(stop[i])
  * after it on the call's stream, for i < n; *count holds how many launches
- * were recorded.  Kernel names: route_logits, route_topk, group, prep,
- * ffn_gateup, ffn_down (small tiles), ffn_gateup_large, ffn_down_large,
- * combine.  The caller owns the events and must keep
- * them, and count, alive while tracing; n <= 0 switches tracing off. */
+ * were recorded.  Kernel names: route_logits, route_topk, group, prep, front
+ * (selection to operands in one launch, small batches), ffn_gateup, ffn_down
+ * (small tiles), ffn_gateup_large, ffn_down_large, combine.  The caller owns
+ * the events and must keep them, and count, alive while tracing; n <= 0
+ * switches tracing off. */
 moe_status moe_trace_kernel(const char* name, hipEvent_t* start, hipEvent_t* stop, int32_t n, int32_t* count);
+
+/* As moe_trace_kernel, recording only launches 0, every, 2 every, ... of the
+ * kernel (every >= 1), so that the events disturb few of the traced steps. */
+moe_status moe_trace_kernel_every(const char* name, hipEvent_t* start, hipEvent_t* stop, int32_t n,
+                                  int32_t every, int32_t* count);
 
 /* ---- host helpers (no device access) ---------------------------------- */
 

@@ -64,7 +64,8 @@ def _load():
     L.moe_share_tables.argtypes = [vp, i32, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int32)]
     L.moe_plan_check.argtypes = [vp, i32, i32]
     L.moe_trace_kernel.argtypes = [ctypes.c_char_p, vp, vp, i32, ctypes.POINTER(ctypes.c_int32)]
-    for f in ("moe_trace_kernel", "moe_workspace_size", "moe_route", "moe_group_tokens", "moe_expert_forward", "moe_combine",
+    L.moe_trace_kernel_every.argtypes = [ctypes.c_char_p, vp, vp, i32, i32, ctypes.POINTER(ctypes.c_int32)]
+    for f in ("moe_trace_kernel", "moe_trace_kernel_every", "moe_workspace_size", "moe_route", "moe_group_tokens", "moe_expert_forward", "moe_combine",
               "moe_layer_forward",
               "moe_planar_bytes", "moe_pack_planar", "moe_place_lpt", "moe_share_tables", "moe_plan_check"):
         getattr(L, f).restype = ctypes.c_int
@@ -75,7 +76,7 @@ lib = _load()
 
 EXPORTS = ("moe_last_error", "moe_version", "moe_workspace_size", "moe_route", "moe_group_tokens",
            "moe_expert_forward", "moe_combine", "moe_layer_forward", "moe_planar_bytes", "moe_pack_planar", "moe_place_lpt",
-           "moe_share_tables", "moe_plan_check", "moe_trace_kernel")
+           "moe_share_tables", "moe_plan_check", "moe_trace_kernel", "moe_trace_kernel_every")
 
 
 def last_error() -> str:
@@ -184,14 +185,16 @@ def share_tables(owner: np.ndarray, share: int, local_order: Optional[np.ndarray
 
 
 class KernelTrace:
-    """Live per-kernel timing: HIP events around each launch of one kernel.
+    """Live per-kernel timing: HIP events around launches 0, every, 2 every, ... of one kernel
+    (at most n of them).
 
-    with KernelTrace("gemv_gateup", n) as tr: ...launches...; then tr.times_ms()"""
+    with KernelTrace("ffn_gateup", n) as tr: ...launches...; then tr.times_ms()"""
 
-    def __init__(self, name: str, n: int):
+    def __init__(self, name: str, n: int, every: int = 1):
         import torch
         self.name = name.encode()
         self.n = n
+        self.every = every
         self._ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         self._ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         for e in self._ev0 + self._ev1:
@@ -202,7 +205,8 @@ class KernelTrace:
         self.count = ctypes.c_int32(0)
 
     def __enter__(self):
-        _check(lib.moe_trace_kernel(self.name, self._h0, self._h1, self.n, ctypes.byref(self.count)))
+        _check(lib.moe_trace_kernel_every(self.name, self._h0, self._h1, self.n, self.every,
+                                          ctypes.byref(self.count)))
         return self
 
     def __exit__(self, *exc):

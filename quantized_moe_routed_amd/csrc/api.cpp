@@ -88,6 +88,9 @@ struct Trace {
   hipEvent_t* start = nullptr;
   hipEvent_t* stop = nullptr;
   int n = 0;
+  int every = 1;       // record launches 0, every, 2 every, ...
+  int seen = 0;        // launches of the kernel since tracing was set
+  bool armed = false;  // the current launch is being recorded
   int32_t* count = nullptr;
 };
 thread_local Trace g_trace;
@@ -178,32 +181,47 @@ moe_status check_qmat(const moe_qmat& m, const char* name, int rows, int cols, b
 namespace moe {
 void trace_pre(const char* name, hipStream_t s) {
   Trace& t = g_trace;
-  if (t.n > 0 && *t.count < t.n && t.name == name) (void)hipEventRecord(t.start[*t.count], s);
+  if (t.n > 0 && t.name == name) {
+    t.armed = t.seen % t.every == 0 && *t.count < t.n;
+    if (t.armed) (void)hipEventRecord(t.start[*t.count], s);
+  }
 }
 void trace_post(const char* name, hipStream_t s) {
   Trace& t = g_trace;
-  if (t.n > 0 && *t.count < t.n && t.name == name) {
-    (void)hipEventRecord(t.stop[*t.count], s);
-    ++*t.count;
+  if (t.n > 0 && t.name == name) {
+    if (t.armed) {
+      (void)hipEventRecord(t.stop[*t.count], s);
+      ++*t.count;
+      t.armed = false;
+    }
+    ++t.seen;
   }
 }
 }  // namespace moe
 
 extern "C" {
 
-moe_status moe_trace_kernel(const char* name, hipEvent_t* start, hipEvent_t* stop, int32_t n, int32_t* count) {
+moe_status moe_trace_kernel_every(const char* name, hipEvent_t* start, hipEvent_t* stop, int32_t n, int32_t every,
+                                  int32_t* count) {
   if (n <= 0) {
     g_trace = Trace{};
     return ok();
   }
   if (!name || !start || !stop || !count) return fail(MOE_ERR_ARG, "moe_trace_kernel: NULL argument");
+  if (every < 1) return fail(MOE_ERR_ARG, "moe_trace_kernel_every: every = %d", every);
+  g_trace = Trace{};
   g_trace.name = name;
   g_trace.start = start;
   g_trace.stop = stop;
   g_trace.n = n;
+  g_trace.every = every;
   g_trace.count = count;
   *count = 0;
   return ok();
+}
+
+moe_status moe_trace_kernel(const char* name, hipEvent_t* start, hipEvent_t* stop, int32_t n, int32_t* count) {
+  return moe_trace_kernel_every(name, start, stop, n, 1, count);
 }
 
 const char* moe_last_error(void) { return g_err.c_str(); }
