@@ -12,6 +12,7 @@
 #include "../../include/moe.h"
 #include "device.h"
 #include "launch.h"
+#include "smallsel.h"
 
 namespace {
 
@@ -517,16 +518,45 @@ moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, in
     if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: group launch");
     return ok();
   }
-  if (T <= moe::kFrontMaxTokens) {
+  moe::SelArgs sel{};
+  if (T <= moe::kSelMaxTokens && E <= moe::kSelMaxE && f.a.max_large == 0) {
+    // router launch (with the operands), then the gate/up launch selects and groups by itself
+    int S = 0;
+    const moe::PrepOut po{f.a.nb32H, const_cast<uint16_t*>(f.a.xq_hi), const_cast<uint16_t*>(f.a.xq_lo),
+                          const_cast<uint16_t*>(f.a.sq_hi), const_cast<uint16_t*>(f.a.sq_lo),
+                          const_cast<float*>(f.a.sigma)};
+    e = moe::launch_logits(x, xt, T, H, router->fmt, qm(*router), bias, ws, &S, s, &po);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: logits launch");
+    sel.z = reinterpret_cast<const float*>(ws);
+    sel.bias = bias;
+    sel.T = T;
+    sel.E = E;
+    sel.k = k;
+    sel.E_local = E_local;
+    sel.g2l = g2l;
+    sel.max_tiles = f.tl.max_small;
+    sel.ids = ids;
+    sel.w = w;
+    sel.counts = counts;
+    sel.offsets = offsets;
+    sel.slot_list = slot_list;
+    sel.n_tiles = f.tl.n_small;
+    sel.tiles = f.tl.small;
+    sel.tile_tok = f.tl.small_tok;
+    f.a.sel = &sel;
+  } else if (T <= moe::kFrontMaxTokens) {
     const size_t lds = moe::front_lds_bytes(T, E, k);
     if (lds > 160 * 1024) return fail(MOE_ERR_UNSUPPORTED, "%s: E = %d needs %zu bytes of LDS", fn, E, lds);
     int S = 0;
-    e = moe::launch_logits(x, xt, T, H, router->fmt, qm(*router), bias, ws, &S, s);
+    const moe::PrepOut po{f.a.nb32H, const_cast<uint16_t*>(f.a.xq_hi), const_cast<uint16_t*>(f.a.xq_lo),
+                          const_cast<uint16_t*>(f.a.sq_hi), const_cast<uint16_t*>(f.a.sq_lo),
+                          const_cast<float*>(f.a.sigma)};
+    // the operands ride on the router's launch (batches this small take the one-expert-per-wave
+    // logits kernel)
+    e = moe::launch_logits(x, xt, T, H, router->fmt, qm(*router), bias, ws, &S, s, &po);
     if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: logits launch");
     e = moe::launch_front(reinterpret_cast<const float*>(ws), S, bias, T, E, k, ids, w, counts, offsets, slot_list, x,
-                          xt, H, f.a.nb32H, const_cast<uint16_t*>(f.a.xq_hi), const_cast<uint16_t*>(f.a.xq_lo),
-                          const_cast<uint16_t*>(f.a.sq_hi), const_cast<uint16_t*>(f.a.sq_lo),
-                          const_cast<float*>(f.a.sigma), f.tl, s);
+                          xt, H, nullptr, f.tl, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: selection launch");
   } else {
     e = moe::launch_route(x, xt, T, H, router->fmt, qm(*router), bias, k, ids, w, ws, s);

@@ -3,6 +3,7 @@
 #pragma once
 #include "device.h"
 #include "fmt.h"
+#include "smallsel.h"
 
 namespace moe {
 
@@ -23,6 +24,7 @@ struct FfnTileArgs {
   FragConsts kc;
   uint16_t *h_hi, *h_lo, *hs_hi, *hs_lo;
   float* y;
+  SelArgs sel;                      // SEL launches: selection inputs and routing outputs
 };
 
 // The d values of one row in one unit (at p): 8 fp16 (Q2SM) or 2 fp16 (Q8_0, in .x).

@@ -27,6 +27,7 @@
 #include "fmt.h"
 #include "launch.h"
 #include "ffn.h"
+#include "smallsel.h"
 
 namespace moe {
 
@@ -37,7 +38,10 @@ constexpr int kStageRows = 4;     // slots per tile; their activation rows are s
 
 // ONE: every tile holds a single slot (one token in the batch), so only the
 // first component of each output fragment is ever needed.
-template <int F, int NM, bool LO, int MODE, bool ONE>
+// SEL (gate/up of batches of at most kSelMaxTokens tokens): the workgroup first selects, groups
+// and numbers the tiles itself from the finished logits (smallsel.h); workgroup (0, 0) stores the
+// routing results and the tile list for the later launches.
+template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL>
 __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a) {
   constexpr int UB = Codes<F>::kUnitBlocks;
   constexpr int CH = NM == 2 ? 2 : (F == FMT_Q8_0 ? 4 : 1);   // units whose loads are issued together
@@ -45,11 +49,20 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   __shared__ float s_sig[16];
 
   const int tile = blockIdx.y;
-  if (tile >= *a.n_tiles) return;
-  const int4 tl = a.tiles[tile];
+  int4 tl, tk;
+  if constexpr (SEL) {
+    __shared__ SelLds sl;
+    small_select<kFfnThreads>(a.sel, sl, blockIdx.x == 0 && blockIdx.y == 0, tile);
+    if (tile >= sl.n_tiles) return;
+    tl = sl.tile;
+    tk = sl.tok;
+  } else {
+    if (tile >= *a.n_tiles) return;
+    tl = a.tiles[tile];
+    // operand rows of the tile: tokens (gate/up, listed with the tile) or grouped positions (down)
+    tk = MODE == MODE_GATEUP ? a.tile_tok[tile] : make_int4(tl.y, tl.y + 1, tl.y + 2, tl.y + 3);
+  }
   const int le = tl.x, p0 = tl.y, rows = tl.z;
-  // operand rows of the tile: tokens (gate/up, listed with the tile) or grouped positions (down)
-  const int4 tk = MODE == MODE_GATEUP ? a.tile_tok[tile] : make_int4(p0, p0 + 1, p0 + 2, p0 + 3);
   auto row_of = [&](int m) { return m == 0 ? tk.x : m == 1 ? tk.y : m == 2 ? tk.z : tk.w; };
   const int n0 = blockIdx.x * 16 * kNT;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -304,12 +317,12 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   }
 }
 
-template <int F, int NM, bool LO, int MODE, bool ONE>
+template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL = false>
 static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_t s) {
   const size_t stage = (size_t)t.stage_rows * t.K * 2 * (LO ? 2 : 1) + (size_t)t.K * 2;
   const size_t red = (size_t)kFfnWaves * kNT * NM * 4 * kWave * 4 + 16 * 33 * 4;
   const size_t lds = stage > red ? stage : red;
-  auto kern = ffn_small_kernel<F, NM, LO, MODE, ONE>;
+  auto kern = ffn_small_kernel<F, NM, LO, MODE, ONE, SEL>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -335,12 +348,20 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   const bool one = a.T == 1;
 #define MOE_SMALL(F, NM, LO, MODE) \
   (one ? launch_small_t<F, NM, LO, MODE, true>(t, a.max_small, s) : launch_small_t<F, NM, LO, MODE, false>(t, a.max_small, s))
+#define MOE_SMALL_SEL(F, LO)                                                                        \
+  (one ? launch_small_t<F, 2, LO, MODE_GATEUP, true, true>(t, a.max_small, s)                       \
+       : launch_small_t<F, 2, LO, MODE_GATEUP, false, true>(t, a.max_small, s))
   t.tiles = a.small; t.tile_tok = a.small_tok; t.n_tiles = a.n_small;
   trace_pre("ffn_gateup", s);
-  if (a.fg == FMT_Q2SM)
+  if (a.sel) {
+    t.sel = *a.sel;
+    if (a.fg == FMT_Q2SM) err = lo ? MOE_SMALL_SEL(FMT_Q2SM, true) : MOE_SMALL_SEL(FMT_Q2SM, false);
+    else err = lo ? MOE_SMALL_SEL(FMT_Q8_0, true) : MOE_SMALL_SEL(FMT_Q8_0, false);
+  } else if (a.fg == FMT_Q2SM) {
     err = lo ? MOE_SMALL(FMT_Q2SM, 2, true, MODE_GATEUP) : MOE_SMALL(FMT_Q2SM, 2, false, MODE_GATEUP);
-  else
+  } else {
     err = lo ? MOE_SMALL(FMT_Q8_0, 2, true, MODE_GATEUP) : MOE_SMALL(FMT_Q8_0, 2, false, MODE_GATEUP);
+  }
   trace_post("ffn_gateup", s);
   if (err != hipSuccess) return err;
   if (a.max_large > 0) {
@@ -365,6 +386,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
     err = launch_large(t, a.fd, MODE_DOWN, true, a.max_large, s);
     trace_post("ffn_down_large", s);
   }
+#undef MOE_SMALL_SEL
 #undef MOE_SMALL
   return err;
 }

@@ -7,6 +7,7 @@
 namespace moe {
 
 struct QMat;
+struct SelArgs;   // smallsel.h
 
 // Optional event tracing of one kernel (see moe_trace_kernel): record an event
 // on the stream before and after the launch of kernel `name`.
@@ -16,10 +17,18 @@ void trace_post(const char* name, hipStream_t s);
 hipError_t launch_route(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
                         int k, int32_t* ids, float* w, void* ws, hipStream_t s);
 size_t route_ws_need(int T, int E, int H, int fmt);   // workspace bytes of launch_route
+// Outputs of the expert operand preparation (prep.h) of every token.
+struct PrepOut {
+  int nb32;
+  uint16_t *xq_hi, *xq_lo, *sq_hi, *sq_lo;
+  float* sigma;
+};
 // The logits alone, into ws: finished logits (*S = 0) or S partial sums per (token, expert) whose
-// pairwise sum plus the bias is the logit (*S > 0); the selection kernels take either.
+// pairwise sum plus the bias is the logit (*S > 0); the selection kernels take either.  With prep,
+// the same launch also prepares every token's expert operand (only where the logits are finished:
+// batches below the token-per-lane router's size).
 hipError_t launch_logits(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
-                         void* ws, int* S, hipStream_t s);
+                         void* ws, int* S, hipStream_t s, const PrepOut* prep);
 
 hipError_t launch_group(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
                         int32_t* slot_list, hipStream_t s);
@@ -44,10 +53,10 @@ struct TileLists {
 // activation operands in one launch (prep.hip), after launch_logits.
 constexpr int kFrontMaxTokens = 8;
 size_t front_lds_bytes(int T, int E, int k);
+// prep: also prepare the operands (NULL: the router's launch did).
 hipError_t launch_front(const float* z, int S, const float* bias, int T, int E, int k, int32_t* ids, float* w,
                         int32_t* counts, int32_t* offsets, int32_t* slot_list, const void* x, int act, int H,
-                        int nb32, uint16_t* xq_hi, uint16_t* xq_lo, uint16_t* sq_hi, uint16_t* sq_lo, float* sigma,
-                        const TileLists& tl, hipStream_t s);
+                        const PrepOut* prep, const TileLists& tl, hipStream_t s);
 
 // Arguments of the expert FFN launches (workspace pointers included).
 struct FfnArgs {
@@ -62,6 +71,10 @@ struct FfnArgs {
   const float* sigma;
   uint16_t *h_hi, *h_lo, *hs_hi, *hs_lo;
   float* y;
+  // non-NULL: the gate/up launch selects, groups and numbers the small tiles itself from finished
+  // logits (batches of at most kSelMaxTokens tokens, no large tiles) and stores the routing
+  // results; small, small_tok and n_small are then its outputs
+  const SelArgs* sel;
 };
 
 // Tile lists + fp16 activation operand (fmt.h) in one launch.

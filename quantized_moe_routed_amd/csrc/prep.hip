@@ -1,27 +1,15 @@
 // Preparation launch of the expert forward: the tile list over the owned
 // experts that received slots (workgroup 0) and the fp16 activation operand
-// of every token (one workgroup per token).
-//
-// Activation operand of token t for a gate/up format F (see fmt.h):
-//   sigma_t = 2^(9-E), E the smallest integer with max_i |x[t,i]| < 2^E
-//             (1 for an all-zero token), so that |x| * sigma * 2^6 < 2^15;
-//   A'[t][32b+8g+e] = x[t][32b+8g+frag_val(e)] * sigma_t * 2^6        (hi, lo)
-//   S'[t][b]        = sigma_t * sum_{i<32} x[t][32b+i]               (hi, lo)
-// The block sums are taken in index order in fp32; blocks past H/32 up to
-// the padded count are zero.
+// of every token (one workgroup per token, prep.h).
 #include "device.h"
 #include "fmt.h"
 #include "launch.h"
+#include "prep.h"
 #include "select.h"
 
 namespace moe {
 
 constexpr int kPrepThreads = 1024;
-
-template <int ACT>
-__device__ __forceinline__ float act_at(const void* x, int64_t i) {
-  return load_act<ACT>(x, i);
-}
 
 // Tiles of bm slots over the owned experts with lo_n <= slots < hi_n that
 // received slots, in ascending global id: tile i covers grouped positions
@@ -73,60 +61,6 @@ __device__ void build_tiles(const int32_t* __restrict__ counts, const int32_t* _
 }
 
 template <int ACT>
-__device__ void prep_token(const void* __restrict__ x, int t, int H, int nb32, uint16_t* __restrict__ xq_hi,
-                           uint16_t* __restrict__ xq_lo, uint16_t* __restrict__ sq_hi, uint16_t* __restrict__ sq_lo,
-                           float* __restrict__ sigma) {
-  __shared__ float wmax[kPrepThreads / kWave];
-  __shared__ float s_sigma;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int64_t row = (int64_t)t * H;
-  float mx = 0.0f;
-  for (int i = tid; i < H; i += kPrepThreads) mx = fmaxf(mx, fabsf(act_at<ACT>(x, row + i)));
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m, kWave));
-  if (lane == 0) wmax[wave] = mx;
-  __syncthreads();
-  if (tid == 0) {
-    float m = 0.0f;
-    for (int w = 0; w < kPrepThreads / kWave; ++w) m = fmaxf(m, wmax[w]);
-    int e = 0;
-    if (m > 0.0f) (void)frexpf(m, &e);   // m = f * 2^e, f in [0.5, 1): m < 2^e
-    const float sg = ldexpf(1.0f, 9 - e);
-    s_sigma = sg;
-    sigma[t] = sg;
-  }
-  __syncthreads();
-  const float sg = s_sigma;
-  const int nb = H / 32;
-  // one thread per (block, K-group): 8 operand values
-  for (int j = tid; j < nb * 4; j += kPrepThreads) {
-    const int b = j >> 2, g = j & 3;
-    uint32_t hi[8], lo[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = act_at<ACT>(x, row + 32 * b + 8 * g + frag_val(e)) * sg * 64.0f;
-      split_f16(v, hi[e], lo[e]);
-    }
-    const int64_t o = row + 32 * b + 8 * g;
-    *reinterpret_cast<uint4*>(xq_hi + o) =
-        make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
-    if (xq_lo)
-      *reinterpret_cast<uint4*>(xq_lo + o) =
-          make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
-  }
-  for (int b = tid; b < nb32; b += kPrepThreads) {
-    uint32_t hi = 0, lo = 0;
-    if (b < nb) {
-      float s = 0.0f;
-      for (int i = 0; i < 32; ++i) s += act_at<ACT>(x, row + 32 * b + i);
-      split_f16(s * sg, hi, lo);
-    }
-    sq_hi[(int64_t)t * nb32 + b] = (uint16_t)hi;
-    sq_lo[(int64_t)t * nb32 + b] = (uint16_t)lo;
-  }
-}
-
-template <int ACT>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const void* __restrict__ x, int T, int H, int nb32,
                                                             uint16_t* __restrict__ xq_hi, uint16_t* __restrict__ xq_lo,
                                                             uint16_t* __restrict__ sq_hi, uint16_t* __restrict__ sq_lo,
@@ -139,7 +73,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const void* __restri
                 tl.max_large, tl.large, tl.n_large, wave_tot);
   } else {
     const int t = blockIdx.x - 1;
-    if (t < T) prep_token<ACT>(x, t, H, nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma);
+    if (t < T) prep_token<ACT, kPrepThreads>(x, t, H, nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma);
   }
 }
 
@@ -161,7 +95,7 @@ hipError_t launch_prep(const void* x, int act, int fmt, int T, int H, int nb32, 
 // expert (a direct stable counting sort of at most 8 k slots) and builds the tile lists, keeping
 // ids, counts, offsets and the slot list in LDS between the steps (each step reads what other
 // threads wrote); the other workgroups prepare one token's operand each, which does not depend on
-// the routing.
+// the routing (when the router's launch has not prepared them already).
 template <int EPL, int ACT>
 __global__ __launch_bounds__(kPrepThreads) void front_kernel(const float* __restrict__ z, int S,
                                                              const float* __restrict__ bias, int T, int E, int k,
@@ -173,7 +107,7 @@ __global__ __launch_bounds__(kPrepThreads) void front_kernel(const float* __rest
                                                              uint16_t* __restrict__ xq_lo, uint16_t* __restrict__ sq_hi,
                                                              uint16_t* __restrict__ sq_lo, float* __restrict__ sigma,
                                                              TileLists tl) {
-  extern __shared__ int32_t fsm[];   // counts [E], offsets [E + 1], ids [T k], slots [T k]
+  extern __shared__ int32_t fsm[];   // counts [E], offsets [E + 1], ids [T k], slots [T k], g2l [E]
   __shared__ int32_t wave_tot[kPrepThreads / kWave];
   if (blockIdx.x == 0) {
     const int tid = threadIdx.x, wave = tid / kWave, n = T * k;
@@ -181,7 +115,11 @@ __global__ __launch_bounds__(kPrepThreads) void front_kernel(const float* __rest
     int32_t* s_off = s_cnt + E;
     int32_t* s_ids = s_off + E + 1;
     int32_t* s_slot = s_ids + n;
+    int32_t* s_g2l = s_slot + n;
+    // the ownership table is fetched now and lands in LDS after the selection
+    const int g2l_e = tid < E ? (tl.g2l ? tl.g2l[tid] : tid) : 0;
     for (int t = wave; t < T; t += kPrepThreads / kWave) topk_token<EPL>(z, S, bias, T, E, k, t, ids, w, s_ids);
+    if (tid < E) s_g2l[tid] = g2l_e;
     __syncthreads();
     // the stable counting sort of a few slots, directly: expert e's count and offset are the slots
     // with id e and with a smaller id; slot i goes to (slots with a smaller id) + (earlier slots
@@ -218,24 +156,28 @@ __global__ __launch_bounds__(kPrepThreads) void front_kernel(const float* __rest
       if (e < E) counts[e] = s_cnt[e];
       offsets[e] = s_off[e];
     }
-    build_tiles(s_cnt, s_off, tl.g2l, E, tl.E_local, tl.n_slots, tl.bm_small, 1, tl.large_min, tl.max_small,
+    build_tiles(s_cnt, s_off, s_g2l, E, tl.E_local, tl.n_slots, tl.bm_small, 1, tl.large_min, tl.max_small,
                 tl.small, tl.n_small, wave_tot, tl.small_tok, s_slot, k);
-    build_tiles(s_cnt, s_off, tl.g2l, E, tl.E_local, tl.n_slots, tl.bm_large, tl.large_min, 0x7FFFFFFF, tl.max_large,
-                tl.large, tl.n_large, wave_tot);
+    if (tl.max_large > 0)   // (batches this small have no large tiles; their count is never read)
+      build_tiles(s_cnt, s_off, s_g2l, E, tl.E_local, tl.n_slots, tl.bm_large, tl.large_min, 0x7FFFFFFF,
+                  tl.max_large, tl.large, tl.n_large, wave_tot);
   } else {
     const int t = blockIdx.x - 1;
-    if (t < T) prep_token<ACT>(x, t, H, nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma);
+    if (t < T) prep_token<ACT, kPrepThreads>(x, t, H, nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma);
   }
 }
 
-size_t front_lds_bytes(int T, int E, int k) { return sizeof(int32_t) * (2 * (size_t)E + 1 + 2 * (size_t)T * k); }
+size_t front_lds_bytes(int T, int E, int k) { return sizeof(int32_t) * (3 * (size_t)E + 1 + 2 * (size_t)T * k); }
 
 hipError_t launch_front(const float* z, int S, const float* bias, int T, int E, int k, int32_t* ids, float* w,
                         int32_t* counts, int32_t* offsets, int32_t* slot_list, const void* x, int act, int H,
-                        int nb32, uint16_t* xq_hi, uint16_t* xq_lo, uint16_t* sq_hi, uint16_t* sq_lo, float* sigma,
-                        const TileLists& tl, hipStream_t s) {
+                        const PrepOut* prep, const TileLists& tl, hipStream_t s) {
+  const PrepOut po = prep ? *prep : PrepOut{};
+  const int nb32 = po.nb32;
+  uint16_t *xq_hi = po.xq_hi, *xq_lo = po.xq_lo, *sq_hi = po.sq_hi, *sq_lo = po.sq_lo;
+  float* sigma = po.sigma;
   const size_t lds = front_lds_bytes(T, E, k);
-  const dim3 grid(1 + T);
+  const dim3 grid(1 + (prep ? T : 0));
 #define MOE_FRONT(EPL, A)                                                                                       \
   do {                                                                                                          \
     auto kern = front_kernel<EPL, A>;                                                                           \

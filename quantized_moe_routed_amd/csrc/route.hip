@@ -19,6 +19,7 @@
 #include "fmt.h"
 #include "launch.h"
 #include "select.h"
+#include "prep.h"
 
 namespace moe {
 
@@ -99,7 +100,14 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
                                                            const void* __restrict__ codes,
                                                            const void* __restrict__ scales,
                                                            const float* __restrict__ bias, int E,
-                                                           float* __restrict__ z) {
+                                                           float* __restrict__ z, PrepOut po) {
+  // workgroups past the logits' ones (first row only) prepare one token's expert operand each
+  const int n_logit_wg = (E + 3) / 4;
+  if ((int)blockIdx.x >= n_logit_wg) {
+    if (blockIdx.y == 0)
+      prep_token<ACT, 256>(x, blockIdx.x - n_logit_wg, H, po.nb32, po.xq_hi, po.xq_lo, po.sq_hi, po.sq_lo, po.sigma);
+    return;
+  }
   const int lane = threadIdx.x % kWave;
   const int e = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (e >= E) return;
@@ -397,27 +405,29 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 
 template <int FMT, int ACT>
 static hipError_t launch_logits_c(int C, const void* x, int T, int H, const QMat& r, const float* bias,
-                                  float* z, hipStream_t s) {
+                                  float* z, const PrepOut& po, hipStream_t s) {
   const int E = r.rows;
-  dim3 grid((E + 3) / 4, (T + kRouteTokTile - 1) / kRouteTokTile);
+  dim3 grid((E + 3) / 4 + (po.xq_hi ? T : 0), (T + kRouteTokTile - 1) / kRouteTokTile);
   switch (C) {
-    case 1: route_logits_kernel<FMT, ACT, 1><<<grid, 256, 0, s>>>(x, T, H, r.codes, r.scales, bias, E, z); break;
-    case 2: route_logits_kernel<FMT, ACT, 2><<<grid, 256, 0, s>>>(x, T, H, r.codes, r.scales, bias, E, z); break;
-    case 4: route_logits_kernel<FMT, ACT, 4><<<grid, 256, 0, s>>>(x, T, H, r.codes, r.scales, bias, E, z); break;
-    case 8: route_logits_kernel<FMT, ACT, 8><<<grid, 256, 0, s>>>(x, T, H, r.codes, r.scales, bias, E, z); break;
+    case 1: route_logits_kernel<FMT, ACT, 1><<<grid, 256, 0, s>>>(x, T, H, r.codes, r.scales, bias, E, z, po); break;
+    case 2: route_logits_kernel<FMT, ACT, 2><<<grid, 256, 0, s>>>(x, T, H, r.codes, r.scales, bias, E, z, po); break;
+    case 4: route_logits_kernel<FMT, ACT, 4><<<grid, 256, 0, s>>>(x, T, H, r.codes, r.scales, bias, E, z, po); break;
+    case 8: route_logits_kernel<FMT, ACT, 8><<<grid, 256, 0, s>>>(x, T, H, r.codes, r.scales, bias, E, z, po); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_logits(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
-                         void* ws, int* S_out, hipStream_t s) {
+                         void* ws, int* S_out, hipStream_t s, const PrepOut* prep) {
+  const PrepOut po = prep ? *prep : PrepOut{};
   const int E = router.rows;
   const bool q8 = fmt == FMT_Q8_0;
   hipError_t err = hipSuccess;
   const LanesPlan lp = lanes_plan(T, E, H, fmt);
   float* z = reinterpret_cast<float*>(ws);
   int S = 0;
+  if (lp.use && po.xq_hi) return hipErrorInvalidValue;   // operands ride only on the small-batch launch
   if (lp.use) {
     const dim3 grid((T + 63) / 64, (lp.groups + kLanesWaves - 1) / kLanesWaves, lp.S);
     trace_pre("route_logits", s);
@@ -434,11 +444,11 @@ hipError_t launch_logits(const void* x, int act, int T, int H, int fmt, const QM
     while (C * kWave < nb) C <<= 1;
     trace_pre("route_logits", s);
     if (act == ACT_F32) {
-      err = q8 ? launch_logits_c<FMT_Q8_0, ACT_F32>(C, x, T, H, router, bias, z, s)
-               : launch_logits_c<FMT_F32, ACT_F32>(C, x, T, H, router, bias, z, s);
+      err = q8 ? launch_logits_c<FMT_Q8_0, ACT_F32>(C, x, T, H, router, bias, z, po, s)
+               : launch_logits_c<FMT_F32, ACT_F32>(C, x, T, H, router, bias, z, po, s);
     } else {
-      err = q8 ? launch_logits_c<FMT_Q8_0, ACT_BF16>(C, x, T, H, router, bias, z, s)
-               : launch_logits_c<FMT_F32, ACT_BF16>(C, x, T, H, router, bias, z, s);
+      err = q8 ? launch_logits_c<FMT_Q8_0, ACT_BF16>(C, x, T, H, router, bias, z, po, s)
+               : launch_logits_c<FMT_F32, ACT_BF16>(C, x, T, H, router, bias, z, po, s);
     }
     trace_post("route_logits", s);
   }
@@ -450,7 +460,7 @@ hipError_t launch_route(const void* x, int act, int T, int H, int fmt, const QMa
                         int k, int32_t* ids, float* w, void* ws, hipStream_t s) {
   const int E = router.rows;
   int S = 0;
-  hipError_t err = launch_logits(x, act, T, H, fmt, router, bias, ws, &S, s);
+  hipError_t err = launch_logits(x, act, T, H, fmt, router, bias, ws, &S, s, nullptr);
   if (err != hipSuccess) return err;
   const float* z = reinterpret_cast<const float*>(ws);
   dim3 grid((T + 3) / 4);

@@ -35,6 +35,29 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
   return op(op(r0, r1), op(r2, r3));
 }
 
+// Wave-wide maximum of an unsigned 64-bit value, in every lane: the two halves travel by DPP, the
+// rows of 16 are reduced by quad and row permutes, then row 0's result is broadcast into row 1
+// and rows 0-1's into rows 2-3, and lane 63 holds the maximum.
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v, uint64_t o) { return o > v ? o : v; }
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_step_u64(uint64_t v) {
+  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xF, false);
+  return dpp_max_u64(v, ((uint64_t)ohi << 32) | olo);
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_step_u64<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+  v = dpp_step_u64<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+  v = dpp_step_u64<0x141, 0xF>(v);   // row_half_mirror
+  v = dpp_step_u64<0x140, 0xF>(v);   // row_mirror: every lane of a row holds the row's maximum
+  v = dpp_step_u64<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_step_u64<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // One wave per token: k rounds, each a wave max of the logit key over the
 // untaken experts followed by a wave min of the expert index among those that
 // hold it (ties go to the lower index).  Weights: s_j = sigmoid(z_j) in fp64
@@ -75,29 +98,28 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ z, int S, c
     const uint32_t kv = float_key(logit_of<EPL>(z, S, bias, T, E, t, min(e, E - 1)));   // loaded unconditionally
     key[i] = live[i] ? kv : 0u;
   }
+  // one wave maximum per round over (key, ~expert): the largest key, ties to the lower expert
   int my_id = -1;
   uint32_t my_key = 0;
   for (int j = 0; j < k; ++j) {
-    uint32_t lk = 0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (live[i] && key[i] > lk) lk = key[i];
-    const uint32_t mk = wave_reduce_u32<true>(lk);
-    uint32_t li = 0xFFFFFFFFu;
+    uint64_t best = 0;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      const uint32_t e = (uint32_t)(i * kWave + lane);
-      if (live[i] && key[i] == mk && e < li) li = e;
+      const uint64_t c = ((uint64_t)key[i] << 32) | (uint32_t)~(uint32_t)(i * kWave + lane);
+      if (live[i] && c > best) best = c;
     }
-    const uint32_t me = wave_reduce_u32<false>(li);
+    const uint64_t mx = wave_max_u64(best);
+    const uint32_t me = ~(uint32_t)mx;
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
       if ((uint32_t)(i * kWave + lane) == me) live[i] = false;
     if (lane == j) {
       my_id = (int)me;
-      my_key = mk;
+      my_key = (uint32_t)(mx >> 32);
     }
   }
+  if (lane < k && ids_copy) ids_copy[t * k + lane] = my_id;
+  if (!w) return;   // ids only (ids may be NULL too)
   const double my_s = 1.0 / (1.0 + exp(-(double)key_to_float(my_key)));
   double ssum = 0.0;
   for (int j = 0; j < k; ++j) {
@@ -106,9 +128,8 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ z, int S, c
     ssum += __longlong_as_double(((long long)(uint32_t)hi << 32) | (uint32_t)lo);
   }
   if (lane < k) {
-    ids[(int64_t)t * k + lane] = my_id;
+    if (ids) ids[(int64_t)t * k + lane] = my_id;
     w[(int64_t)t * k + lane] = (float)(my_s / ssum);
-    if (ids_copy) ids_copy[t * k + lane] = my_id;
   }
 }
 

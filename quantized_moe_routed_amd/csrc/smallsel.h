@@ -1,0 +1,123 @@
+// Selection, grouping and small-tile list of a batch of at most kSelMaxTokens
+// tokens, computed by one workgroup entirely in LDS (internal to libmoe).
+//
+// Every workgroup of the gate/up launch of such a batch runs it on the finished
+// logits, so that no launch of its own stands between the router and the
+// expert kernel; the workgroup that is marked as the writer also stores the
+// results (ids, weights, counts, offsets, slot list, tile list) for the later
+// launches.  The results equal those of the separate kernels: the same top-k
+// (select.h), the stable counting sort of the slots by expert, and tiles of up
+// to 4 slots over the owned experts that received slots, in ascending global
+// id, capped at max_tiles.
+#pragma once
+#include "device.h"
+#include "select.h"
+
+namespace moe {
+
+constexpr int kSelMaxTokens = 8;
+constexpr int kSelMaxE = 256;    // experts: 4 per lane of a wave
+constexpr int kSelTile = 4;      // slots per small tile
+
+struct SelArgs {
+  const float* z;                // [T][E] finished logits
+  const float* bias;
+  int T, E, k, E_local;
+  const int32_t* g2l;            // NULL: every expert owned, local = global
+  int max_tiles;
+  int32_t *ids, *counts, *offsets, *slot_list, *n_tiles;
+  float* w;
+  int4 *tiles, *tile_tok;
+};
+
+struct SelLds {
+  int32_t ids[kSelMaxTokens * 32];
+  int32_t slot[kSelMaxTokens * 32];
+  int32_t cnt[kSelMaxE], off[kSelMaxE + 1], g2l[kSelMaxE];
+  int32_t wave_tot[16];
+  int4 tile, tok;
+  int32_t n_tiles;
+};
+
+// want: the tile whose description lands in L.tile / L.tok (when want < L.n_tiles).
+template <int NT>
+__device__ __forceinline__ void small_select(const SelArgs& a, SelLds& L, bool writer, int want) {
+  static_assert(NT >= kSelMaxE && NT % kWave == 0, "one thread per expert");
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int E = a.E, k = a.k, n = a.T * a.k;
+  const int g2l_e = tid < E ? (a.g2l ? a.g2l[tid] : tid) : -1;   // lands in LDS after the selection
+  for (int t = wave; t < a.T; t += NT / kWave)
+    topk_token<4>(a.z, 0, a.bias, a.T, E, k, t, writer ? a.ids : nullptr, writer ? a.w : nullptr, L.ids);
+  if (tid < E) L.g2l[tid] = g2l_e;
+  __syncthreads();
+  // stable counting sort of the n slots: expert e's count and offset are the slots with id e and
+  // with a smaller id; slot i goes to (slots with a smaller id) + (earlier slots with its id)
+  int c = 0, o = 0;
+  if (tid < E) {
+    for (int i = 0; i < n; ++i) {
+      const int v = L.ids[i];
+      c += v == tid;
+      o += (unsigned)v < (unsigned)tid;
+    }
+    L.cnt[tid] = c;
+    L.off[tid] = o;
+    if (tid == E - 1) L.off[E] = o + c;
+  }
+  if (tid < n) {
+    const int v = L.ids[tid];
+    if ((unsigned)v < (unsigned)E) {
+      int r = 0;
+      for (int j = 0; j < n; ++j) {
+        const int u = L.ids[j];
+        r += (unsigned)u < (unsigned)v || (u == v && j < tid);
+      }
+      L.slot[r] = tid;
+    }
+  }
+  // tiles of up to 4 slots per owned expert that received slots, numbered in ascending id
+  const int le = tid < E ? g2l_e : -1;
+  const int mt = (c > 0 && le >= 0 && le < a.E_local) ? (c + kSelTile - 1) / kSelTile : 0;
+  int incl = mt;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int u = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += u;
+  }
+  if (lane == kWave - 1) L.wave_tot[wave] = incl;
+  __syncthreads();   // also: slot list, counts and offsets complete
+  int base = incl - mt;
+  for (int w = 0; w < wave; ++w) base += L.wave_tot[w];
+  if (tid == 0) {
+    int tot = 0;
+    for (int w = 0; w < NT / kWave; ++w) tot += L.wave_tot[w];
+    L.n_tiles = min(tot, a.max_tiles);
+    if (writer) *a.n_tiles = min(tot, a.max_tiles);
+  }
+  for (int i = 0; i < mt; ++i) {
+    const int ti = base + i;
+    if (ti >= a.max_tiles) break;
+    const int rows = min(kSelTile, c - kSelTile * i), p0 = o + kSelTile * i;
+    int r[kSelTile];
+#pragma unroll
+    for (int j = 0; j < kSelTile; ++j) r[j] = j < rows ? L.slot[p0 + j] / k : 0;
+    const int4 tl = make_int4(le, p0, rows, tid), tk = make_int4(r[0], r[1], r[2], r[3]);
+    if (ti == want) {
+      L.tile = tl;
+      L.tok = tk;
+    }
+    if (writer) {
+      a.tiles[ti] = tl;
+      a.tile_tok[ti] = tk;
+    }
+  }
+  if (writer) {
+    for (int i = tid; i < n; i += NT) a.slot_list[i] = L.slot[i];
+    for (int e = tid; e <= E; e += NT) {
+      if (e < E) a.counts[e] = L.cnt[e];
+      a.offsets[e] = L.off[e];
+    }
+  }
+  __syncthreads();
+}
+
+}  // namespace moe

@@ -299,10 +299,12 @@ def test_layer_call_equals_the_four_calls(torch, cfg, T):
         assert np.array_equal(a, b), f"{name} differs between the layer call and the four calls"
 
 
-def test_layer_call_owned_share(torch):
-    """The layer call with an owned-expert table (a share of the experts): the four calls' partial."""
-    _say("layer call vs four calls: cfg5 share, T=24")
-    wl = synth.make(5, T=24)
+@pytest.mark.parametrize("T", [5, 24])
+def test_layer_call_owned_share(torch, T):
+    """The layer call with an owned-expert table (a share of the experts): the four calls' partial,
+    for a batch that the expert launch routes by itself and for one routed by separate launches."""
+    _say(f"layer call vs four calls: cfg5 share, T={T}")
+    wl = synth.make(5, T=T)
     import quantized_moe_routed_amd as moe
     owner = moe.place_lpt(np.arange(wl.E, dtype=np.int64) % 7 + 1, 2)
     g2l, l2g = moe.share_tables(owner, 0)
