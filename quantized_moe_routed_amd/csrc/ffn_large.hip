@@ -484,15 +484,15 @@ static hipError_t launch_large_t(const FfnTileArgs& t, int max_tiles, hipStream_
   return hipGetLastError();
 }
 
-// Activation operands with a lo plane (fp32 inputs, and h) take two row groups of waves, so
-// that each wave holds half the accumulators.
+// Two row groups of waves (8 waves, two per SIMD): each wave holds half the accumulators, and
+// one wave's matrix products run beside the other's vector work.
 hipError_t launch_large(const FfnTileArgs& t, int fmt, int mode, bool lo, int max_tiles, hipStream_t s) {
   if (mode == MODE_GATEUP) {
     if (fmt == FMT_Q2SM)
       return lo ? launch_large_t<FMT_Q2SM, 2, true, MODE_GATEUP, 1, 2>(t, max_tiles, s)
-                : launch_large_t<FMT_Q2SM, 2, false, MODE_GATEUP, 1, 1>(t, max_tiles, s);
+                : launch_large_t<FMT_Q2SM, 2, false, MODE_GATEUP, 1, 2>(t, max_tiles, s);
     return lo ? launch_large_t<FMT_Q8_0, 2, true, MODE_GATEUP, 1, 2>(t, max_tiles, s)
-              : launch_large_t<FMT_Q8_0, 2, false, MODE_GATEUP, 1, 1>(t, max_tiles, s);
+              : launch_large_t<FMT_Q8_0, 2, false, MODE_GATEUP, 1, 2>(t, max_tiles, s);
   }
   return fmt == FMT_Q2SM ? launch_large_t<FMT_Q2SM, 1, true, MODE_DOWN, 2, 2>(t, max_tiles, s)
                          : launch_large_t<FMT_Q8_0, 1, true, MODE_DOWN, 2, 2>(t, max_tiles, s);
