@@ -223,9 +223,10 @@ def cpu_baseline(budget_s=15.0, max_tokens=400):
 # Kernels whose HBM traffic is recorded from hardware counters, by workload, with the sources that
 # define them (the record is ignored once any of them changes).
 TRAFFIC_KERNELS = {
-    "decode": ("ffn_gateup", "moe::ffn_small_kernel<2, 2, true, 0, true>",
+    "decode": ("ffn_gateup", "moe::ffn_small_kernel<2, 2, true, 0, true, true>",
                ["quantized_moe_routed_amd/csrc/ffn.hip", "quantized_moe_routed_amd/csrc/ffn.h",
-                "quantized_moe_routed_amd/csrc/fmt.h", "quantized_moe_routed_amd/csrc/device.h"]),
+                "quantized_moe_routed_amd/csrc/fmt.h", "quantized_moe_routed_amd/csrc/device.h",
+                "quantized_moe_routed_amd/csrc/smallsel.h", "quantized_moe_routed_amd/csrc/select.h"]),
 }
 COPY_BYTES = 256 << 20   # the calibration copy: reads and writes this many bytes
 

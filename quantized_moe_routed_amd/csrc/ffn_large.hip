@@ -51,7 +51,7 @@ __device__ __forceinline__ void pin(uint4& v) {
 }
 __device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
 
-template <int F, int NM, bool LO, int MODE, int NT2, int WM>
+template <int F, int NM, bool LO, int MODE, int NT2, int WM, int CG>
 struct LargeCfg {
   static constexpr int UB = Codes<F>::kUnitBlocks;
   static constexpr int P = LO ? 2 : 1;                    // activation planes
@@ -59,8 +59,8 @@ struct LargeCfg {
   static constexpr int GU = UB >= SB ? 1 : SB / UB;        // code units per weight-load group
   static constexpr int STAGE = P * SB * kLgRows * 64;     // LDS bytes per stage
   static constexpr int WC = 32 * NT2;                     // output columns per wave
-  static constexpr int BN = 4 * WC;                       // output columns per workgroup
-  static constexpr int NW = 4 * WM;                       // waves: 4 column groups x WM row groups
+  static constexpr int BN = CG * WC;                      // output columns per workgroup
+  static constexpr int NW = CG * WM;                      // waves: CG column groups x WM row groups
   static constexpr int THREADS = 64 * NW;
   static constexpr int MIMAX = 4 / WM;                    // 32-row fragments per wave
   static constexpr int GPW = 8 / NW;                      // 16-row activation groups each wave fetches
@@ -74,10 +74,10 @@ struct LargeCfg {
 // so those blocks add exact zeros.
 // Columns past N (N not a multiple of the workgroup's width) are computed on
 // a repeated column and not stored.
-template <int F, int NM, bool LO, int MODE, int NT2, int WM, int MI>
+template <int F, int NM, bool LO, int MODE, int NT2, int WM, int CG, int MI>
 __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0, int rows, int ct, int r0,
                                            const int32_t* s_slot, const float* s_inv) {
-  using C = LargeCfg<F, NM, LO, MODE, NT2, WM>;
+  using C = LargeCfg<F, NM, LO, MODE, NT2, WM, CG>;
   constexpr int UB = C::UB, P = C::P, SB = C::SB;
   extern __shared__ __align__(16) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -85,7 +85,7 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
   const int c32 = lane & 31, g2 = lane >> 5;
   const int K = a.K, N = a.N, nb = K / 32;
   const int n_units = (nb + UB - 1) / UB;
-  const int n0 = ct * C::BN + (wave & 3) * C::WC;
+  const int n0 = ct * C::BN + (wave % CG) * C::WC;
   const int64_t rbytes = Codes<F>::row_bytes(K);
   const int64_t sbytes = Codes<F>::scale_row_bytes(K);
 
@@ -427,10 +427,10 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
   }
 }
 
-template <int F, int NM, bool LO, int MODE, int NT2, int WM>
-__global__ __launch_bounds__((LargeCfg<F, NM, LO, MODE, NT2, WM>::THREADS), 1) void ffn_large_kernel(FfnTileArgs a,
-                                                                                                   int n_ct) {
-  using C = LargeCfg<F, NM, LO, MODE, NT2, WM>;
+template <int F, int NM, bool LO, int MODE, int NT2, int WM, int CG>
+__global__ __launch_bounds__((LargeCfg<F, NM, LO, MODE, NT2, WM, CG>::THREADS), 1) void ffn_large_kernel(
+    FfnTileArgs a, int n_ct) {
+  using C = LargeCfg<F, NM, LO, MODE, NT2, WM, CG>;
   // workgroup i runs on XCD i mod 8: the column tiles of one slot tile are consecutive on one XCD
   const int id = blockIdx.x, q = id >> 3;
   const int tile = (id & 7) + 8 * (q / n_ct), ct = q % n_ct;
@@ -446,10 +446,10 @@ __global__ __launch_bounds__((LargeCfg<F, NM, LO, MODE, NT2, WM>::THREADS), 1) v
     s_slot[threadIdx.x] = sl;
     s_inv[threadIdx.x] = MODE == MODE_GATEUP ? 1.0f / a.sigma[sl / a.k] : 1.0f;   // a power of two: exact
   }
-  const int wm = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) >> 2;
+  const int wm = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) / CG;
   const int r0 = wm * 32 * C::MIMAX;
   const int mi = min(max((tl.z - r0 + 31) / 32, 0), C::MIMAX);
-#define MOE_TILE(M) large_tile<F, NM, LO, MODE, NT2, WM, M>(a, tl.x, tl.y, tl.z, ct, r0, s_slot, s_inv)
+#define MOE_TILE(M) large_tile<F, NM, LO, MODE, NT2, WM, CG, M>(a, tl.x, tl.y, tl.z, ct, r0, s_slot, s_inv)
   if constexpr (C::MIMAX == 4) {
     switch (mi) {
       case 1: MOE_TILE(1); break;
@@ -467,20 +467,20 @@ __global__ __launch_bounds__((LargeCfg<F, NM, LO, MODE, NT2, WM>::THREADS), 1) v
 #undef MOE_TILE
 }
 
-template <int F, int NM, bool LO, int MODE, int NT2, int WM>
+template <int F, int NM, bool LO, int MODE, int NT2, int WM, int CG>
 static hipError_t launch_large_t(const FfnTileArgs& t, int max_tiles, hipStream_t s) {
-  using C = LargeCfg<F, NM, LO, MODE, NT2, WM>;
+  using C = LargeCfg<F, NM, LO, MODE, NT2, WM, CG>;
   static bool attr_set = false;
   const size_t lds = 2 * (size_t)C::STAGE;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_large_kernel<F, NM, LO, MODE, NT2, WM>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_large_kernel<F, NM, LO, MODE, NT2, WM, CG>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int n_ct = (t.N + C::BN - 1) / C::BN;
   const int grid = 8 * n_ct * ((max_tiles + 7) / 8);
-  ffn_large_kernel<F, NM, LO, MODE, NT2, WM><<<grid, C::THREADS, lds, s>>>(t, n_ct);
+  ffn_large_kernel<F, NM, LO, MODE, NT2, WM, CG><<<grid, C::THREADS, lds, s>>>(t, n_ct);
   return hipGetLastError();
 }
 
@@ -489,13 +489,13 @@ static hipError_t launch_large_t(const FfnTileArgs& t, int max_tiles, hipStream_
 hipError_t launch_large(const FfnTileArgs& t, int fmt, int mode, bool lo, int max_tiles, hipStream_t s) {
   if (mode == MODE_GATEUP) {
     if (fmt == FMT_Q2SM)
-      return lo ? launch_large_t<FMT_Q2SM, 2, true, MODE_GATEUP, 1, 2>(t, max_tiles, s)
-                : launch_large_t<FMT_Q2SM, 2, false, MODE_GATEUP, 1, 2>(t, max_tiles, s);
-    return lo ? launch_large_t<FMT_Q8_0, 2, true, MODE_GATEUP, 1, 2>(t, max_tiles, s)
-              : launch_large_t<FMT_Q8_0, 2, false, MODE_GATEUP, 1, 2>(t, max_tiles, s);
+      return lo ? launch_large_t<FMT_Q2SM, 2, true, MODE_GATEUP, 1, 2, 4>(t, max_tiles, s)
+                : launch_large_t<FMT_Q2SM, 2, false, MODE_GATEUP, 1, 2, 4>(t, max_tiles, s);
+    return lo ? launch_large_t<FMT_Q8_0, 2, true, MODE_GATEUP, 1, 2, 4>(t, max_tiles, s)
+              : launch_large_t<FMT_Q8_0, 2, false, MODE_GATEUP, 1, 2, 4>(t, max_tiles, s);
   }
-  return fmt == FMT_Q2SM ? launch_large_t<FMT_Q2SM, 1, true, MODE_DOWN, 2, 2>(t, max_tiles, s)
-                         : launch_large_t<FMT_Q8_0, 1, true, MODE_DOWN, 2, 2>(t, max_tiles, s);
+  return fmt == FMT_Q2SM ? launch_large_t<FMT_Q2SM, 1, true, MODE_DOWN, 2, 2, 4>(t, max_tiles, s)
+                         : launch_large_t<FMT_Q8_0, 1, true, MODE_DOWN, 2, 2, 4>(t, max_tiles, s);
 }
 
 }  // namespace moe
