@@ -299,10 +299,26 @@ def test_layer_call_equals_the_four_calls(torch, cfg, T):
         assert np.array_equal(a, b), f"{name} differs between the layer call and the four calls"
 
 
-@pytest.mark.parametrize("T", [5, 24])
+@pytest.mark.parametrize("I", [2304, 4096])
+def test_layer_call_one_token_down_widths(torch, I):
+    """One token with 2-bit down weights at two expert widths: the down launch's waves take one or
+    two code units of each expert row; I=2304 (nine units) leaves waves with one unit and waves
+    with none."""
+    _say(f"layer call vs four calls: one token, I={I}")
+    wl = synth.make(synth.custom(1, 2048, 64, I, 8, gate_fmt=synth.FMT_Q2SM, up_fmt=synth.FMT_Q2SM,
+                                 down_fmt=synth.FMT_Q2SM, bias="zipf1.1", name=f"down_w{I}"))
+    layer = make_layer(wl)
+    calls, fused = _run_both(layer, wl, torch)
+    for name, a, b in zip(("ids", "w", "counts", "offsets", "slot_list", "y_slot", "out"), calls, fused):
+        assert np.array_equal(a, b), f"{name} differs between the layer call and the four calls"
+    check_against_oracle(wl, run(layer, wl, torch), oracle_expect(wl), what=f"one token I={I}")
+
+
+@pytest.mark.parametrize("T", [1, 5, 24])
 def test_layer_call_owned_share(torch, T):
     """The layer call with an owned-expert table (a share of the experts): the four calls' partial,
-    for a batch that the expert launch routes by itself and for one routed by separate launches."""
+    for one token, a batch that the expert launch routes by itself, and one routed by separate
+    launches."""
     _say(f"layer call vs four calls: cfg5 share, T={T}")
     wl = synth.make(5, T=T)
     import quantized_moe_routed_amd as moe
