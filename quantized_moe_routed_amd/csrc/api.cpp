@@ -519,7 +519,8 @@ moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, in
     return ok();
   }
   moe::SelArgs sel{};
-  if (T <= moe::kSelMaxTokens && E <= moe::kSelMaxE && f.a.max_large == 0) {
+  if (T <= moe::kSelMaxTokens && E <= moe::kSelMaxE && f.a.max_large == 0 &&
+      moe::logit_ranges(T, E, H, router->fmt) <= moe::kSelMaxRanges) {
     // router launch (with the operands), then the gate/up launch selects and groups by itself
     int S = 0;
     const moe::PrepOut po{f.a.nb32H, const_cast<uint16_t*>(f.a.xq_hi), const_cast<uint16_t*>(f.a.xq_lo),
@@ -528,6 +529,7 @@ moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, in
     e = moe::launch_logits(x, xt, T, H, router->fmt, qm(*router), bias, ws, &S, s, &po);
     if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: logits launch");
     sel.z = reinterpret_cast<const float*>(ws);
+    sel.S = S;
     sel.bias = bias;
     sel.T = T;
     sel.E = E;
@@ -544,7 +546,7 @@ moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, in
     sel.tiles = f.tl.small;
     sel.tile_tok = f.tl.small_tok;
     f.a.sel = &sel;
-  } else if (T <= moe::kFrontMaxTokens) {
+  } else if (T <= moe::kFrontMaxTokens && moe::logit_ranges(T, E, H, router->fmt) <= moe::kSelMaxRanges) {
     const size_t lds = moe::front_lds_bytes(T, E, k);
     if (lds > 160 * 1024) return fail(MOE_ERR_UNSUPPORTED, "%s: E = %d needs %zu bytes of LDS", fn, E, lds);
     int S = 0;

@@ -17,6 +17,7 @@ void trace_post(const char* name, hipStream_t s);
 hipError_t launch_route(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
                         int k, int32_t* ids, float* w, void* ws, hipStream_t s);
 size_t route_ws_need(int T, int E, int H, int fmt);   // workspace bytes of launch_route
+int logit_ranges(int T, int E, int H, int fmt);       // partial sums per (token, expert) of the logits launch
 // Outputs of the expert operand preparation (prep.h) of every token.
 struct PrepOut {
   int nb32;

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kPrepThreads) void front_kernel(const float* __rest
     int32_t* s_g2l = s_slot + n;
     // the ownership table is fetched now and lands in LDS after the selection
     const int g2l_e = tid < E ? (tl.g2l ? tl.g2l[tid] : tid) : 0;
-    for (int t = wave; t < T; t += kPrepThreads / kWave) topk_token<EPL>(z, S, bias, T, E, k, t, ids, w, s_ids);
+    for (int t = wave; t < T; t += kPrepThreads / kWave) topk_token<EPL, kSelMaxRanges>(z, S, bias, T, E, k, t, ids, w, s_ids);
     if (tid < E) s_g2l[tid] = g2l_e;
     __syncthreads();
     // the stable counting sort of a few slots, directly: expert e's count and offset are the slots

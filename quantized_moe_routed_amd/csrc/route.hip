@@ -34,43 +34,51 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 constexpr int kRouteTokTile = 16;
 
-// The C blocks lane*C .. lane*C+C-1 of router row e as floats (int8 codes or fp32 weights) and their
-// scales d (Q8_0; 0 for blocks past the row); blocks past nb are zero.
-template <int FMT, int C>
-__device__ __forceinline__ void load_router_blocks(const void* __restrict__ codes, const void* __restrict__ scales,
-                                                   int e, int H, int lane, float (&wv)[C][32], float (&dsc)[C]) {
+// The 32 activations of one block as fp32 (fp32 or bf16 input).
+template <int ACT>
+__device__ __forceinline__ void load_x_block(const void* __restrict__ x, int64_t off, float (&xv)[32]) {
+  if constexpr (ACT == ACT_F32) {
+    const float4* x4 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 v = x4[i];
+      xv[4 * i] = v.x;
+      xv[4 * i + 1] = v.y;
+      xv[4 * i + 2] = v.z;
+      xv[4 * i + 3] = v.w;
+    }
+  } else {
+    const uint4* x4 = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = x4[i];
+      const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xv[8 * i + 2 * q] = __uint_as_float(wds[q] << 16);
+        xv[8 * i + 2 * q + 1] = __uint_as_float(wds[q] & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
+// The C blocks lane*C .. lane*C+C-1 of fp32 router row e; blocks past H/32 are zero.
+template <int C>
+__device__ __forceinline__ void load_router_blocks(const float* __restrict__ codes, int e, int H, int lane,
+                                                   float (&wv)[C][32]) {
   const int nb = H / 32;
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     const int b = lane * C + j;
-    dsc[j] = 0.0f;
     if (b < nb) {
-      if constexpr (FMT == FMT_Q8_0) {
-        // row-group layout: block b's values 8g..8g+7 in unit b/2 of row e, group g, half b%2
-        const int nu = (nb + 1) / 2;
-        const int8_t* q = reinterpret_cast<const int8_t*>(codes) + code_off(e, b >> 1, nu) + (b & 1) * 8;
-        int words[8];
+      const float4* w4 = reinterpret_cast<const float4*>(codes + (int64_t)e * H + b * 32);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int2 v = *reinterpret_cast<const int2*>(q + 16 * g);
-          words[2 * g] = v.x;
-          words[2 * g + 1] = v.y;
-        }
-#pragma unroll
-        for (int i = 0; i < 32; ++i) wv[j][i] = (float)(int8_t)(words[i / 4] >> (8 * (i % 4)));
-        dsc[j] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(
-            reinterpret_cast<const uint8_t*>(scales) + Codes<FMT_Q8_0>::d_off(e, b >> 1, nu) + 2 * (b & 1)));
-      } else {
-        const float4* w4 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(codes) +
-                                                           (int64_t)e * H + b * 32);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float4 v = w4[i];
-          wv[j][4 * i] = v.x;
-          wv[j][4 * i + 1] = v.y;
-          wv[j][4 * i + 2] = v.z;
-          wv[j][4 * i + 3] = v.w;
-        }
+      for (int i = 0; i < 8; ++i) {
+        const float4 v = w4[i];
+        wv[j][4 * i] = v.x;
+        wv[j][4 * i + 1] = v.y;
+        wv[j][4 * i + 2] = v.z;
+        wv[j][4 * i + 3] = v.w;
       }
     } else {
 #pragma unroll
@@ -95,10 +103,11 @@ __device__ __forceinline__ float tree_sum(float (&r)[C]) {
 }
 
 
-template <int FMT, int ACT, int C>
+// fp32 router: one expert per wave, C blocks per lane; per token the block chains, then the tree
+// (its first levels in the lane, the rest across the wave), plus the bias.
+template <int ACT, int C>
 __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restrict__ x, int T, int H,
                                                            const void* __restrict__ codes,
-                                                           const void* __restrict__ scales,
                                                            const float* __restrict__ bias, int E,
                                                            float* __restrict__ z, PrepOut po) {
   // workgroups past the logits' ones (first row only) prepare one token's expert operand each
@@ -114,8 +123,7 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
   const int nb = H / 32;
 
   float wv[C][32];
-  float dsc[C];
-  load_router_blocks<FMT, C>(codes, scales, e, H, lane, wv, dsc);
+  load_router_blocks<C>(reinterpret_cast<const float*>(codes), e, H, lane, wv);
   const float be = bias ? bias[e] : 0.0f;
 
   const int t0 = blockIdx.y * kRouteTokTile;
@@ -128,39 +136,99 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
       r[j] = 0.0f;
       if (b < nb) {
         float xv[32];
-        if constexpr (ACT == ACT_F32) {
-          const float4* x4 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) +
-                                                             (int64_t)t * H + b * 32);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            float4 v = x4[i];
-            xv[4 * i] = v.x;
-            xv[4 * i + 1] = v.y;
-            xv[4 * i + 2] = v.z;
-            xv[4 * i + 3] = v.w;
-          }
-        } else {
-          const uint4* x4 = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) +
-                                                           (int64_t)t * H + b * 32);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            uint4 v = x4[i];
-            uint32_t wds[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              xv[8 * i + 2 * q] = __uint_as_float(wds[q] << 16);
-              xv[8 * i + 2 * q + 1] = __uint_as_float(wds[q] & 0xFFFF0000u);
-            }
-          }
-        }
+        load_x_block<ACT>(x, (int64_t)t * H + b * 32, xv);
         float p = 0.0f;
 #pragma unroll
         for (int i = 0; i < 32; ++i) p = __builtin_fmaf(wv[j][i], xv[i], p);
-        r[j] = (FMT == FMT_Q8_0) ? dsc[j] * p : p;
+        r[j] = p;
       }
     }
     const float v = tree_sum<C>(r);
     if (lane == 0) z[(int64_t)t * E + e] = bias ? v + be : v;
+  }
+}
+
+// ---- few tokens, Q8_0 router: a wave per 16 experts -----------------------------------------
+// A wave takes one row group of the router (16 experts, whose rows lie side by side in each
+// 1 KB unit) and kRgUnits consecutive units (two blocks each); lane (s, r) holds the 64 bytes
+// of row r in unit s, read as four 16-byte loads, and the x blocks it needs are the same for the
+// 16 lanes of a unit.  Per token and lane: the two blocks' chains in index order, times d; the
+// two blocks added (tree level 1), then units in pairs across lanes (levels 2 and 3), then the
+// waves of the workgroup in pairs through LDS.  A workgroup covers one aligned range of
+// kRgBlocks blocks and writes its subtree sum zp[range][t][e]; the ranges' sums (the tree's top
+// levels) and the bias are added by the selection.  Blocks past H/32 count as zero.
+constexpr int kRgWaves = 4;
+constexpr int kRgUnits = 4;
+constexpr int kRgBlocks = 2 * kRgUnits * kRgWaves;
+
+static int rg_ranges(int H) { return (H / 32 + kRgBlocks - 1) / kRgBlocks; }
+
+template <int ACT>
+__global__ __launch_bounds__(kRgWaves * kWave) void route_logits_rg_kernel(const void* __restrict__ x, int T, int H,
+                                                                            const void* __restrict__ codes,
+                                                                            const void* __restrict__ scales, int E,
+                                                                            int S, float* __restrict__ zp,
+                                                                            PrepOut po) {
+  // workgroups past the S ranges (first row group and token tile only) prepare one token's
+  // expert operand each
+  if ((int)blockIdx.x >= S) {
+    if (blockIdx.y == 0 && blockIdx.z == 0)
+      prep_token<ACT, kRgWaves * kWave>(x, blockIdx.x - S, H, po.nb32, po.xq_hi, po.xq_lo, po.sq_hi, po.sq_lo,
+                                        po.sigma);
+    return;
+  }
+  __shared__ float part[kRouteTokTile][kRgWaves][16];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int r = lane & 15, su = lane >> 4;
+  const int nb = H / 32, nu = (nb + 1) / 2;
+  const int e = blockIdx.y * 16 + r, ec = min(e, E - 1);
+  const int u = ((int)blockIdx.x * kRgWaves + wave) * kRgUnits + su, uc = min(u, nu - 1);
+  const int b0 = 2 * u, b1 = 2 * u + 1;
+  // every load is issued (rows past E and units past the row read the last ones and are dropped)
+  const uint8_t* cp = reinterpret_cast<const uint8_t*>(codes) + code_off(ec, uc, nu);
+  uint4 c[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) c[g] = *reinterpret_cast<const uint4*>(cp + 16 * g);
+  const uint32_t dd = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(scales) +
+                                                         Codes<FMT_Q8_0>::d_off(ec, uc, nu));
+  const float d0 = half_bits_to_float((uint16_t)(dd & 0xFFFFu)), d1 = half_bits_to_float((uint16_t)(dd >> 16));
+  // group g holds values 8g..8g+7 of block b0 (words x, y) and of block b1 (words z, w)
+  float w0[32], w1[32];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t a[4] = {c[g].x, c[g].y, c[g].z, c[g].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      w0[8 * g + i] = (float)(int8_t)(a[i / 4] >> (8 * (i % 4)));
+      w1[8 * g + i] = (float)(int8_t)(a[2 + i / 4] >> (8 * (i % 4)));
+    }
+  }
+  const int t0 = blockIdx.z * kRouteTokTile;
+  const int nt = min(T - t0, kRouteTokTile);
+  for (int tl = 0; tl < nt; ++tl) {
+    const int64_t row = (int64_t)(t0 + tl) * H;
+    float x0[32], x1[32];
+    load_x_block<ACT>(x, row + 32 * min(b0, nb - 1), x0);
+    load_x_block<ACT>(x, row + 32 * min(b1, nb - 1), x1);
+    float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      p0 = __builtin_fmaf(w0[i], x0[i], p0);
+      p1 = __builtin_fmaf(w1[i], x1[i], p1);
+    }
+    const float r0 = b0 < nb ? d0 * p0 : 0.0f;
+    const float r1 = b1 < nb ? d1 * p1 : 0.0f;
+    float v = r0 + r1;
+    v = v + __shfl_xor(v, 16, kWave);
+    v = v + __shfl_xor(v, 32, kWave);
+    if (su == 0) part[tl][wave][r] = v;
+  }
+  __syncthreads();
+  static_assert(kRgWaves == 4, "the workgroup's tree below has two levels");
+  if (tid < nt * 16 && e < E) {
+    const int tl = tid >> 4;
+    const float v = (part[tl][0][r] + part[tl][1][r]) + (part[tl][2][r] + part[tl][3][r]);
+    zp[((int64_t)blockIdx.x * T + t0 + tl) * E + e] = v;
   }
 }
 
@@ -208,9 +276,15 @@ static LanesPlan lanes_plan(int T, int E, int H, int fmt) {
   return p;
 }
 
-size_t route_ws_need(int T, int E, int H, int fmt) {
+// partial sums per (token, expert) that the logits launch writes (0: finished logits)
+int logit_ranges(int T, int E, int H, int fmt) {
   const LanesPlan p = lanes_plan(T, E, H, fmt);
-  return (size_t)(p.use ? p.S : 1) * T * E * sizeof(float);
+  if (p.use) return p.S;
+  return fmt == FMT_Q8_0 ? rg_ranges(H) : 0;
+}
+
+size_t route_ws_need(int T, int E, int H, int fmt) {
+  return (size_t)std::max(1, logit_ranges(T, E, H, fmt)) * T * E * sizeof(float);
 }
 
 // p += w(lane 16 r + N) * x  (fused, one rounding).  A DPP operand must not have been written by
@@ -403,16 +477,16 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   if (t < T) topk_token<EPL>(z, S, bias, T, E, k, t, ids, w);
 }
 
-template <int FMT, int ACT>
+template <int ACT>
 static hipError_t launch_logits_c(int C, const void* x, int T, int H, const QMat& r, const float* bias,
                                   float* z, const PrepOut& po, hipStream_t s) {
   const int E = r.rows;
   dim3 grid((E + 3) / 4 + (po.xq_hi ? T : 0), (T + kRouteTokTile - 1) / kRouteTokTile);
   switch (C) {
-    case 1: route_logits_kernel<FMT, ACT, 1><<<grid, 256, 0, s>>>(x, T, H, r.codes, r.scales, bias, E, z, po); break;
-    case 2: route_logits_kernel<FMT, ACT, 2><<<grid, 256, 0, s>>>(x, T, H, r.codes, r.scales, bias, E, z, po); break;
-    case 4: route_logits_kernel<FMT, ACT, 4><<<grid, 256, 0, s>>>(x, T, H, r.codes, r.scales, bias, E, z, po); break;
-    case 8: route_logits_kernel<FMT, ACT, 8><<<grid, 256, 0, s>>>(x, T, H, r.codes, r.scales, bias, E, z, po); break;
+    case 1: route_logits_kernel<ACT, 1><<<grid, 256, 0, s>>>(x, T, H, r.codes, bias, E, z, po); break;
+    case 2: route_logits_kernel<ACT, 2><<<grid, 256, 0, s>>>(x, T, H, r.codes, bias, E, z, po); break;
+    case 4: route_logits_kernel<ACT, 4><<<grid, 256, 0, s>>>(x, T, H, r.codes, bias, E, z, po); break;
+    case 8: route_logits_kernel<ACT, 8><<<grid, 256, 0, s>>>(x, T, H, r.codes, bias, E, z, po); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -438,18 +512,24 @@ hipError_t launch_logits(const void* x, int act, int T, int H, int fmt, const QM
     trace_post("route_logits", s);
     err = hipGetLastError();
     S = lp.S;
-  } else {
+  } else if (q8) {
+    S = rg_ranges(H);
+    if (S > kMaxRanges) return hipErrorInvalidValue;
+    const dim3 grid(S + (po.xq_hi ? T : 0), (E + 15) / 16, (T + kRouteTokTile - 1) / kRouteTokTile);
+    trace_pre("route_logits", s);
+    if (act == ACT_F32)
+      route_logits_rg_kernel<ACT_F32><<<grid, kRgWaves * kWave, 0, s>>>(x, T, H, router.codes, router.scales, E, S, z, po);
+    else
+      route_logits_rg_kernel<ACT_BF16><<<grid, kRgWaves * kWave, 0, s>>>(x, T, H, router.codes, router.scales, E, S, z, po);
+    trace_post("route_logits", s);
+    err = hipGetLastError();
+  } else {   // fp32 router
     const int nb = H / 32;
     int C = 1;
     while (C * kWave < nb) C <<= 1;
     trace_pre("route_logits", s);
-    if (act == ACT_F32) {
-      err = q8 ? launch_logits_c<FMT_Q8_0, ACT_F32>(C, x, T, H, router, bias, z, po, s)
-               : launch_logits_c<FMT_F32, ACT_F32>(C, x, T, H, router, bias, z, po, s);
-    } else {
-      err = q8 ? launch_logits_c<FMT_Q8_0, ACT_BF16>(C, x, T, H, router, bias, z, po, s)
-               : launch_logits_c<FMT_F32, ACT_BF16>(C, x, T, H, router, bias, z, po, s);
-    }
+    err = act == ACT_F32 ? launch_logits_c<ACT_F32>(C, x, T, H, router, bias, z, po, s)
+                         : launch_logits_c<ACT_BF16>(C, x, T, H, router, bias, z, po, s);
     trace_post("route_logits", s);
   }
   *S_out = S;

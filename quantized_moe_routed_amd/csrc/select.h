@@ -6,6 +6,7 @@
 namespace moe {
 
 constexpr int kMaxRanges = 32;   // partial logits per (token, expert): block ranges of the router
+constexpr int kSelMaxRanges = 8;  // ranges taken by the selections inside the small-batch launches
 
 // Order-preserving unsigned key of a logit: larger z -> larger key, -0 and +0
 // equal, NaN -> 0 (below every number).  key_to_float inverts it (0 -> NaN).
@@ -58,46 +59,74 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// One wave per token: k rounds, each a wave max of the logit key over the
-// untaken experts followed by a wave min of the expert index among those that
-// hold it (ties go to the lower index).  Weights: s_j = sigmoid(z_j) in fp64
-// on lane j, their sum taken in slot order by every lane, w_j = s_j / sum.
-// With S > 0 the logits arrive as S partial sums per (token, expert) (block ranges, zp[s][t][e]),
-// added here pairwise, level by level, and then the bias is added; with S == 0, z holds finished
-// logits.
-template <int EPL>  // experts per lane (E <= 64 * EPL)
-__device__ __forceinline__ float logit_of(const float* __restrict__ z, int S, const float* __restrict__ bias,
-                                          int T, int E, int t, int e) {
-  if (S == 0) return z[(int64_t)t * E + e];
-  // every load is issued (ranges past S read range S - 1 and are dropped): none behind a branch
-  float v[kMaxRanges];
+// Order-preserving keys of the lane's experts i * 64 + lane (0 and not live past E).  The logit
+// of (t, e): with M == 0 z holds it (bias included); otherwise the S <= M partial sums are added
+// pairwise, level by level, and then the bias.  Every load of every expert is issued before any
+// is used: ranges past S read range S - 1 and experts past E read expert E - 1, both dropped, and
+// with no bias the bias load reads z and is dropped.
+template <int EPL, int M>
+__device__ __forceinline__ void logit_keys(const float* __restrict__ z, int S, const float* __restrict__ bias,
+                                           int T, int E, int t, int lane, uint32_t (&key)[EPL],
+                                           bool (&live)[EPL]) {
+  int ec[EPL];
 #pragma unroll
-  for (int i = 0; i < kMaxRanges; ++i) {
-    const float p = z[((int64_t)min(i, S - 1) * T + t) * E + e];
-    v[i] = i < S ? p : 0.0f;
+  for (int i = 0; i < EPL; ++i) {
+    live[i] = i * kWave + lane < E;
+    ec[i] = min(i * kWave + lane, E - 1);
+  }
+  float zl[EPL];
+  if constexpr (M == 0) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) zl[i] = z[(int64_t)t * E + ec[i]];
+  } else {
+    float v[EPL][M], bv[EPL];
+    const float* bp = bias ? bias : z;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+#pragma unroll
+      for (int j = 0; j < M; ++j) v[i][j] = z[((int64_t)min(j, S - 1) * T + t) * E + ec[i]];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) bv[i] = bp[ec[i]];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+#pragma unroll
+      for (int w = 1; w < M; w <<= 1)
+#pragma unroll
+        for (int j = 0; j + w < M; j += 2 * w) v[i][j] = j + w < S ? v[i][j] + v[i][j + w] : v[i][j];
+      zl[i] = bias ? v[i][0] + bv[i] : v[i][0];
+    }
   }
 #pragma unroll
-  for (int w = 1; w < kMaxRanges; w <<= 1)
-#pragma unroll
-    for (int i = 0; i + w < kMaxRanges; i += 2 * w)
-      if (i + w < S) v[i] = v[i] + v[i + w];
-  return bias ? v[0] + bias[e] : v[0];
+  for (int i = 0; i < EPL; ++i) key[i] = live[i] ? float_key(zl[i]) : 0u;
 }
 
-template <int EPL>  // experts per lane (E <= 64 * EPL)
+// Keys from M partial ranges, M the first of M0, 2 M0, ... that holds S, at most MAXS.
+template <int EPL, int M, int MAXS>
+__device__ __forceinline__ void logit_keys_upto(const float* __restrict__ z, int S, const float* __restrict__ bias,
+                                                int T, int E, int t, int lane, uint32_t (&key)[EPL],
+                                                bool (&live)[EPL]) {
+  if constexpr (M >= MAXS) {
+    logit_keys<EPL, MAXS>(z, S, bias, T, E, t, lane, key, live);
+  } else {
+    if (S <= M) logit_keys<EPL, M>(z, S, bias, T, E, t, lane, key, live);
+    else logit_keys_upto<EPL, 2 * M, MAXS>(z, S, bias, T, E, t, lane, key, live);
+  }
+}
+
+// One wave per token: k rounds, each one wave maximum of (logit key, complement of the expert
+// index) over the untaken experts, i.e. the largest logit with ties to the lower index.
+// Weights: s_j = sigmoid(z_j) in fp64 on lane j, their sum taken in slot order by every lane,
+// w_j = s_j / sum.  With S > 0 the logits arrive as S partial sums per (token, expert) over
+// aligned block ranges (zp[s][t][e]); with S == 0, z holds finished logits.
+template <int EPL, int MAXS = kMaxRanges>  // experts per lane (E <= 64 * EPL); S <= MAXS
 __device__ __forceinline__ void topk_token(const float* __restrict__ z, int S, const float* __restrict__ bias, int T,
                                            int E, int k, int t, int32_t* __restrict__ ids, float* __restrict__ w,
                                            int32_t* ids_copy = nullptr) {
   const int lane = threadIdx.x % kWave;
   uint32_t key[EPL];
   bool live[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = i * kWave + lane;
-    live[i] = e < E;
-    const uint32_t kv = float_key(logit_of<EPL>(z, S, bias, T, E, t, min(e, E - 1)));   // loaded unconditionally
-    key[i] = live[i] ? kv : 0u;
-  }
+  if (S == 0) logit_keys<EPL, 0>(z, S, bias, T, E, t, lane, key, live);
+  else logit_keys_upto<EPL, 4, MAXS>(z, S, bias, T, E, t, lane, key, live);
   // one wave maximum per round over (key, ~expert): the largest key, ties to the lower expert
   int my_id = -1;
   uint32_t my_key = 0;

@@ -17,10 +17,11 @@ namespace moe {
 
 constexpr int kSelMaxTokens = 8;
 constexpr int kSelMaxE = 256;    // experts: 4 per lane of a wave
-constexpr int kSelTile = 4;      // slots per small tile
+constexpr int kSelTile = 4;       // slots per small tile
 
 struct SelArgs {
-  const float* z;                // [T][E] finished logits
+  const float* z;                // [S][T][E] partial logits over aligned block ranges ([T][E] finished ones if S == 0)
+  int S;
   const float* bias;
   int T, E, k, E_local;
   const int32_t* g2l;            // NULL: every expert owned, local = global
@@ -47,7 +48,7 @@ __device__ __forceinline__ void small_select(const SelArgs& a, SelLds& L, bool w
   const int E = a.E, k = a.k, n = a.T * a.k;
   const int g2l_e = tid < E ? (a.g2l ? a.g2l[tid] : tid) : -1;   // lands in LDS after the selection
   for (int t = wave; t < a.T; t += NT / kWave)
-    topk_token<4>(a.z, 0, a.bias, a.T, E, k, t, writer ? a.ids : nullptr, writer ? a.w : nullptr, L.ids);
+    topk_token<4, kSelMaxRanges>(a.z, a.S, a.bias, a.T, E, k, t, writer ? a.ids : nullptr, writer ? a.w : nullptr, L.ids);
   if (tid < E) L.g2l[tid] = g2l_e;
   __syncthreads();
   // stable counting sort of the n slots: expert e's count and offset are the slots with id e and

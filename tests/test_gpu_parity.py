@@ -299,6 +299,40 @@ def test_layer_call_equals_the_four_calls(torch, cfg, T):
         assert np.array_equal(a, b), f"{name} differs between the layer call and the four calls"
 
 
+@pytest.mark.parametrize("k", [1, 5, 8, 9, 17])
+def test_combine_alone(torch, k):
+    """moe_combine by itself, with and without an owner table (some experts unowned, one id past the
+    expert range), H=1000 leaving a partial workgroup.  Dyadic inputs (y in steps of 2^-10 below 1,
+    w in steps of 2^-8) make every product and partial sum exact in fp32, so the sum over the owned
+    slots is known exactly; random inputs are checked against a float64 sum."""
+    import quantized_moe_routed_amd as moe
+    _say(f"combine alone: k={k}")
+    rng = np.random.default_rng(100 + k)
+    T, H, E = 3, 1000, 40
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[0, k - 1] = E + 3
+    g2l = np.where(rng.random(E) < 0.6, np.arange(E), -1).astype(np.int32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    for exact in (True, False):
+        if exact:
+            y = (rng.integers(-1000, 1001, size=(T * k, H)) / 1024.0).astype(np.float32)
+            w = (rng.integers(1, 256, size=(T, k)) / 256.0).astype(np.float32)
+        else:
+            y = rng.standard_normal((T * k, H)).astype(np.float32)
+            w = rng.random((T, k)).astype(np.float32)
+        for table in (None, g2l):
+            own = np.ones((T, k), bool) if table is None else (ids < E) & (table[np.minimum(ids, E - 1)] >= 0)
+            ref = np.einsum("tj,tjh->th", (w * own).astype(np.float64), y.reshape(T, k, H).astype(np.float64))
+            out = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+            moe.combine(dev(y), dev(w), dev(ids), None if table is None else dev(table), T, k, H, E, out)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            if exact:
+                assert np.array_equal(got, ref.astype(np.float32)), f"k={k}, table={table is not None}"
+            else:
+                assert_close(got, ref, what=f"combine k={k}")
+
+
 @pytest.mark.parametrize("I", [2304, 4096])
 def test_layer_call_one_token_down_widths(torch, I):
     """One token with 2-bit down weights at two expert widths: the down launch's waves take one or
