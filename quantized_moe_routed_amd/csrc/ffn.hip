@@ -39,8 +39,14 @@ constexpr int kStageRows = 4;     // slots per tile; their activation rows are s
 // ONE: every tile holds a single slot (one token in the batch), so only the
 // first component of each output fragment is ever needed.
 // SEL (gate/up of batches of at most kSelMaxTokens tokens): the workgroup first selects, groups
-// and numbers the tiles itself from the finished logits (smallsel.h); workgroup (0, 0) stores the
-// routing results and the tile list for the later launches.
+// and numbers the tiles itself from the logits (smallsel.h); one workgroup of an extra grid row
+// stores the routing results and the tile list for the later launches.
+// Bytes of the activation staging area (rows hi [+ lo], then a row of zeros), rounded to 16: the
+// one-token selection keeps its candidates past it.
+__host__ __device__ constexpr size_t sel_cand_offset(int stage_rows, int K, bool lo) {
+  return ((size_t)stage_rows * K * 2 * (lo ? 2 : 1) + (size_t)K * 2 + 15) & ~(size_t)15;
+}
+
 template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL>
 __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a) {
   constexpr int UB = Codes<F>::kUnitBlocks;
@@ -51,11 +57,25 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   const int tile = blockIdx.y;
   int4 tl, tk;
   if constexpr (SEL) {
-    __shared__ SelLds sl;
-    small_select<kFfnThreads>(a.sel, sl, blockIdx.x == 0 && blockIdx.y == 0, tile);
-    if (tile >= sl.n_tiles) return;
-    tl = sl.tile;
-    tk = sl.tok;
+    // the grid's last row holds no tile: its workgroup 0 stores the routing results
+    const bool writer = blockIdx.y == gridDim.y - 1;
+    if (writer && blockIdx.x != 0) return;
+    if constexpr (ONE) {
+      // each wave selects by itself; its candidates sit past the staging area, which faster waves
+      // start to fill while slower ones still select
+      static_assert(kFfnWaves <= kSelMaxTokens, "one candidate area per wave");
+      uint64_t* cand = reinterpret_cast<uint64_t*>(smem + sel_cand_offset(a.stage_rows, a.K, LO)) +
+                       (size_t)(threadIdx.x / kWave) * (a.sel.E + kThrMaxK);
+      tl = tk = make_int4(0, 0, 0, 0);
+      const int n = one_token_select(a.sel, writer, writer ? -1 : tile, cand, tl, tk);
+      if (writer || tile >= n) return;
+    } else {
+      __shared__ SelLds sl;
+      small_select<kFfnThreads>(a.sel, sl, writer, writer ? -1 : tile, reinterpret_cast<uint64_t*>(smem));
+      if (writer || tile >= sl.n_tiles) return;
+      tl = sl.tile;
+      tk = sl.tok;
+    }
   } else {
     if (tile >= *a.n_tiles) return;
     tl = a.tiles[tile];
@@ -321,14 +341,18 @@ template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL = false>
 static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_t s) {
   const size_t stage = (size_t)t.stage_rows * t.K * 2 * (LO ? 2 : 1) + (size_t)t.K * 2;
   const size_t red = (size_t)kFfnWaves * kNT * NM * 4 * kWave * 4 + 16 * 33 * 4;
-  const size_t lds = stage > red ? stage : red;
+  size_t lds = stage > red ? stage : red;
+  if (SEL) {
+    const size_t sel = ONE ? sel_cand_offset(t.stage_rows, t.K, LO) + kSelScratchBytes : kSelScratchBytes;
+    if (lds < sel) lds = sel;
+  }
   auto kern = ffn_small_kernel<F, NM, LO, MODE, ONE, SEL>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  kern<<<dim3(t.N / (16 * kNT), max_tiles), kFfnThreads, lds, s>>>(t);
+  kern<<<dim3(t.N / (16 * kNT), max_tiles + (SEL ? 1 : 0)), kFfnThreads, lds, s>>>(t);
   return hipGetLastError();
 }
 

@@ -107,7 +107,9 @@ __global__ __launch_bounds__(kPrepThreads) void front_kernel(const float* __rest
                                                              uint16_t* __restrict__ xq_lo, uint16_t* __restrict__ sq_hi,
                                                              uint16_t* __restrict__ sq_lo, float* __restrict__ sigma,
                                                              TileLists tl) {
-  extern __shared__ int32_t fsm[];   // counts [E], offsets [E + 1], ids [T k], slots [T k], g2l [E]
+  // counts [E], offsets [E + 1], ids [T k], slots [T k], g2l [E], then (8-byte aligned) the
+  // selection's candidates, E + kThrMaxK per token
+  extern __shared__ __align__(8) int32_t fsm[];
   __shared__ int32_t wave_tot[kPrepThreads / kWave];
   if (blockIdx.x == 0) {
     const int tid = threadIdx.x, wave = tid / kWave, n = T * k;
@@ -118,7 +120,9 @@ __global__ __launch_bounds__(kPrepThreads) void front_kernel(const float* __rest
     int32_t* s_g2l = s_slot + n;
     // the ownership table is fetched now and lands in LDS after the selection
     const int g2l_e = tid < E ? (tl.g2l ? tl.g2l[tid] : tid) : 0;
-    for (int t = wave; t < T; t += kPrepThreads / kWave) topk_token<EPL, kSelMaxRanges>(z, S, bias, T, E, k, t, ids, w, s_ids);
+    uint64_t* s_cand = reinterpret_cast<uint64_t*>(fsm + ((3 * E + 1 + 2 * n + 1) & ~1));
+    for (int t = wave; t < T; t += kPrepThreads / kWave)
+      topk_token<EPL, kSelMaxRanges>(z, S, bias, T, E, k, t, ids, w, s_ids, s_cand + (size_t)t * (E + kThrMaxK));
     if (tid < E) s_g2l[tid] = g2l_e;
     __syncthreads();
     // the stable counting sort of a few slots, directly: expert e's count and offset are the slots
@@ -167,7 +171,10 @@ __global__ __launch_bounds__(kPrepThreads) void front_kernel(const float* __rest
   }
 }
 
-size_t front_lds_bytes(int T, int E, int k) { return sizeof(int32_t) * (3 * (size_t)E + 1 + 2 * (size_t)T * k); }
+size_t front_lds_bytes(int T, int E, int k) {
+  const size_t words = (3 * (size_t)E + 1 + 2 * (size_t)T * k + 1) & ~(size_t)1;
+  return sizeof(int32_t) * words + sizeof(uint64_t) * (size_t)T * (E + kThrMaxK);
+}
 
 hipError_t launch_front(const float* z, int S, const float* bias, int T, int E, int k, int32_t* ids, float* w,
                         int32_t* counts, int32_t* offsets, int32_t* slot_list, const void* x, int act, int H,

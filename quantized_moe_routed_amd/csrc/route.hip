@@ -473,8 +473,10 @@ template <int EPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ z, int S,
                                                          const float* __restrict__ bias, int T, int E, int k,
                                                          int32_t* __restrict__ ids, float* __restrict__ w) {
+  extern __shared__ uint64_t tk_cand[];   // E + kThrMaxK candidates per wave
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (t < T) topk_token<EPL>(z, S, bias, T, E, k, t, ids, w);
+  if (t < T)
+    topk_token<EPL>(z, S, bias, T, E, k, t, ids, w, nullptr, tk_cand + (size_t)(threadIdx.x / kWave) * (E + kThrMaxK));
 }
 
 template <int ACT>
@@ -544,12 +546,13 @@ hipError_t launch_route(const void* x, int act, int T, int H, int fmt, const QMa
   if (err != hipSuccess) return err;
   const float* z = reinterpret_cast<const float*>(ws);
   dim3 grid((T + 3) / 4);
+  const size_t lds = (size_t)4 * (E + kThrMaxK) * sizeof(uint64_t);   // (at most 33 KiB: E <= 1024)
   trace_pre("route_topk", s);
-  if (E <= 64) route_topk_kernel<1><<<grid, 256, 0, s>>>(z, S, bias, T, E, k, ids, w);
-  else if (E <= 128) route_topk_kernel<2><<<grid, 256, 0, s>>>(z, S, bias, T, E, k, ids, w);
-  else if (E <= 256) route_topk_kernel<4><<<grid, 256, 0, s>>>(z, S, bias, T, E, k, ids, w);
-  else if (E <= 512) route_topk_kernel<8><<<grid, 256, 0, s>>>(z, S, bias, T, E, k, ids, w);
-  else route_topk_kernel<16><<<grid, 256, 0, s>>>(z, S, bias, T, E, k, ids, w);
+  if (E <= 64) route_topk_kernel<1><<<grid, 256, lds, s>>>(z, S, bias, T, E, k, ids, w);
+  else if (E <= 128) route_topk_kernel<2><<<grid, 256, lds, s>>>(z, S, bias, T, E, k, ids, w);
+  else if (E <= 256) route_topk_kernel<4><<<grid, 256, lds, s>>>(z, S, bias, T, E, k, ids, w);
+  else if (E <= 512) route_topk_kernel<8><<<grid, 256, lds, s>>>(z, S, bias, T, E, k, ids, w);
+  else route_topk_kernel<16><<<grid, 256, lds, s>>>(z, S, bias, T, E, k, ids, w);
   trace_post("route_topk", s);
   return hipGetLastError();
 }

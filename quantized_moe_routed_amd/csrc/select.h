@@ -75,16 +75,20 @@ __device__ __forceinline__ void logit_keys(const float* __restrict__ z, int S, c
     ec[i] = min(i * kWave + lane, E - 1);
   }
   float zl[EPL];
+  const int tu = __builtin_amdgcn_readfirstlane(t);   // (one token per wave: row bases stay scalar)
   if constexpr (M == 0) {
+    const float* zt = z + (int64_t)tu * E;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) zl[i] = z[(int64_t)t * E + ec[i]];
+    for (int i = 0; i < EPL; ++i) zl[i] = zt[ec[i]];
   } else {
     float v[EPL][M], bv[EPL];
     const float* bp = bias ? bias : z;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i)
+    for (int j = 0; j < M; ++j) {
+      const float* zj = z + ((int64_t)min(j, S - 1) * T + tu) * E;
 #pragma unroll
-      for (int j = 0; j < M; ++j) v[i][j] = z[((int64_t)min(j, S - 1) * T + t) * E + ec[i]];
+      for (int i = 0; i < EPL; ++i) v[i][j] = zj[ec[i]];
+    }
 #pragma unroll
     for (int i = 0; i < EPL; ++i) bv[i] = bp[ec[i]];
 #pragma unroll
@@ -113,23 +117,96 @@ __device__ __forceinline__ void logit_keys_upto(const float* __restrict__ z, int
   }
 }
 
+// Top-k (k <= kThrMaxK) of one wave's keys by a threshold: tau is the smallest of the row maxima
+// (rows of 16 lanes, per key slot) over the rows that hold a live expert, 0 when fewer than k rows
+// do.  Every such row's maximum is at least tau, so at least k live experts have a key >= tau;
+// those candidates go to LDS as composites (key, complement of the expert index), which are all
+// distinct, and a candidate's rank is the number of larger composites.  The k of rank < k, in rank
+// order, are exactly the k largest keys with ties to the lower index.  cand holds E + kThrMaxK
+// entries.  Lanes j < k receive slot j's expert and key.
+constexpr int kThrMaxK = 8;
+
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  return v;
+}
+
+template <int EPL>
+__device__ __forceinline__ void topk_threshold(const uint32_t (&key)[EPL], const bool (&live)[EPL], int E, int k,
+                                               int lane, uint64_t* __restrict__ cand, int& my_id,
+                                               uint32_t& my_key) {
+  uint32_t gm[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) gm[i] = row_max_u32(key[i]);   // keys of experts past E are 0
+  uint32_t tau = 0xFFFFFFFFu;
+  int ng = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (i * kWave + 16 * r < E) {
+        const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)gm[i], 16 * r);
+        tau = v < tau ? v : tau;
+        ++ng;
+      }
+  if (ng < k) tau = 0;
+  int nc = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const bool c = live[i] && key[i] >= tau;
+    const uint64_t m = __ballot(c);
+    if (c) {
+      const int pos = nc + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      cand[pos] = ((uint64_t)key[i] << 32) | (uint32_t)~(uint32_t)(i * kWave + lane);
+    }
+    nc += __popcll(m);
+  }
+  uint64_t* top = cand + E;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  for (int j0 = 0; j0 < nc; j0 += kWave) {
+    const int j = j0 + lane;
+    const uint64_t mine = cand[min(j, nc - 1)];
+    int rank = 0;
+#pragma unroll 4
+    for (int q = 0; q < nc; ++q) rank += cand[q] > mine ? 1 : 0;
+    if (j < nc && rank < k) top[rank] = mine;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane < k) {
+    const uint64_t c = top[lane];
+    my_id = (int)~(uint32_t)c;
+    my_key = (uint32_t)(c >> 32);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // cand is free again for the next call
+}
+
 // One wave per token: k rounds, each one wave maximum of (logit key, complement of the expert
 // index) over the untaken experts, i.e. the largest logit with ties to the lower index.
 // Weights: s_j = sigmoid(z_j) in fp64 on lane j, their sum taken in slot order by every lane,
 // w_j = s_j / sum.  With S > 0 the logits arrive as S partial sums per (token, expert) over
-// aligned block ranges (zp[s][t][e]); with S == 0, z holds finished logits.
+// aligned block ranges (zp[s][t][e]); with S == 0, z holds finished logits.  Given LDS for
+// E + kThrMaxK candidates (cand) and k <= kThrMaxK, the threshold selection above replaces the
+// rounds (same result).
+// The selection itself: lane j < k receives slot j's expert and its logit key.
 template <int EPL, int MAXS = kMaxRanges>  // experts per lane (E <= 64 * EPL); S <= MAXS
-__device__ __forceinline__ void topk_token(const float* __restrict__ z, int S, const float* __restrict__ bias, int T,
-                                           int E, int k, int t, int32_t* __restrict__ ids, float* __restrict__ w,
-                                           int32_t* ids_copy = nullptr) {
+__device__ __forceinline__ void topk_lanes(const float* __restrict__ z, int S, const float* __restrict__ bias, int T,
+                                           int E, int k, int t, uint64_t* cand, int& my_id, uint32_t& my_key) {
   const int lane = threadIdx.x % kWave;
   uint32_t key[EPL];
   bool live[EPL];
   if (S == 0) logit_keys<EPL, 0>(z, S, bias, T, E, t, lane, key, live);
   else logit_keys_upto<EPL, 4, MAXS>(z, S, bias, T, E, t, lane, key, live);
+  my_id = -1;
+  my_key = 0;
+  if (cand && k <= kThrMaxK) {
+    topk_threshold<EPL>(key, live, E, k, lane, cand, my_id, my_key);
+    return;
+  }
   // one wave maximum per round over (key, ~expert): the largest key, ties to the lower expert
-  int my_id = -1;
-  uint32_t my_key = 0;
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0;
 #pragma unroll
@@ -147,8 +224,13 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ z, int S, c
       my_key = (uint32_t)(mx >> 32);
     }
   }
-  if (lane < k && ids_copy) ids_copy[t * k + lane] = my_id;
-  if (!w) return;   // ids only (ids may be NULL too)
+}
+
+// Routing outputs of token t from the lanes' slots (all lanes of the wave take part): the
+// sigmoids in fp64, their sum in slot order by every lane, w_j = s_j / sum; ids (if given) beside.
+__device__ __forceinline__ void topk_store(int k, int t, int my_id, uint32_t my_key, int32_t* __restrict__ ids,
+                                           float* __restrict__ w) {
+  const int lane = threadIdx.x % kWave;
   const double my_s = 1.0 / (1.0 + exp(-(double)key_to_float(my_key)));
   double ssum = 0.0;
   for (int j = 0; j < k; ++j) {
@@ -160,6 +242,18 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ z, int S, c
     if (ids) ids[(int64_t)t * k + lane] = my_id;
     w[(int64_t)t * k + lane] = (float)(my_s / ssum);
   }
+}
+
+template <int EPL, int MAXS = kMaxRanges>  // experts per lane (E <= 64 * EPL); S <= MAXS
+__device__ __forceinline__ void topk_token(const float* __restrict__ z, int S, const float* __restrict__ bias, int T,
+                                           int E, int k, int t, int32_t* __restrict__ ids, float* __restrict__ w,
+                                           int32_t* ids_copy = nullptr, uint64_t* cand = nullptr) {
+  const int lane = threadIdx.x % kWave;
+  int my_id;
+  uint32_t my_key;
+  topk_lanes<EPL, MAXS>(z, S, bias, T, E, k, t, cand, my_id, my_key);
+  if (lane < k && ids_copy) ids_copy[t * k + lane] = my_id;
+  if (w) topk_store(k, t, my_id, my_key, ids, w);   // (without w nothing more is stored)
 }
 
 }  // namespace moe

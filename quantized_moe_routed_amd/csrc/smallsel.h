@@ -40,15 +40,21 @@ struct SelLds {
   int32_t n_tiles;
 };
 
-// want: the tile whose description lands in L.tile / L.tok (when want < L.n_tiles).
+// LDS for the threshold selection: E + kThrMaxK candidates per token
+constexpr size_t kSelScratchBytes = (size_t)kSelMaxTokens * (kSelMaxE + kThrMaxK) * sizeof(uint64_t);
+
+// want: the tile whose description lands in L.tile / L.tok (when want < L.n_tiles).  scratch:
+// kSelScratchBytes of LDS, free again when the call returns.
 template <int NT>
-__device__ __forceinline__ void small_select(const SelArgs& a, SelLds& L, bool writer, int want) {
+__device__ __forceinline__ void small_select(const SelArgs& a, SelLds& L, bool writer, int want,
+                                             uint64_t* scratch) {
   static_assert(NT >= kSelMaxE && NT % kWave == 0, "one thread per expert");
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int E = a.E, k = a.k, n = a.T * a.k;
   const int g2l_e = tid < E ? (a.g2l ? a.g2l[tid] : tid) : -1;   // lands in LDS after the selection
   for (int t = wave; t < a.T; t += NT / kWave)
-    topk_token<4, kSelMaxRanges>(a.z, a.S, a.bias, a.T, E, k, t, writer ? a.ids : nullptr, writer ? a.w : nullptr, L.ids);
+    topk_token<4, kSelMaxRanges>(a.z, a.S, a.bias, a.T, E, k, t, writer ? a.ids : nullptr, writer ? a.w : nullptr, L.ids,
+                                 scratch + (size_t)t * (E + kThrMaxK));
   if (tid < E) L.g2l[tid] = g2l_e;
   __syncthreads();
   // stable counting sort of the n slots: expert e's count and offset are the slots with id e and
@@ -119,6 +125,78 @@ __device__ __forceinline__ void small_select(const SelArgs& a, SelLds& L, bool w
     }
   }
   __syncthreads();
+}
+
+// One token: its k experts are distinct, so every selected expert holds one slot and, when owned,
+// one tile, and the stable counting sort reduces to ranks.  Each wave selects by itself (cand: its
+// own E + kThrMaxK entries of LDS) and finds its workgroup's tile with no LDS exchange and no
+// barrier: slot j's position is the number of selected ids below id_j, its tile number the number
+// of owned selected ids below id_j (tiles in ascending expert id, as in small_select).  Wave 0 of
+// the writer stores what small_select stores for one token.  Returns the tile count; tl / tk
+// receive tile want when want is below it.
+__device__ __forceinline__ int one_token_select(const SelArgs& a, bool writer, int want, uint64_t* cand,
+                                                int4& tl, int4& tk) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int E = a.E, k = a.k;
+  // ownership table in registers, fetched ahead of the selection: expert i * 64 + lane in slot i
+  // (without a table the load reads the logits and is dropped)
+  const int32_t* gp = a.g2l ? a.g2l : reinterpret_cast<const int32_t*>(a.z);
+  int g2l_r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = i * kWave + lane;
+    const int v = gp[min(e, E - 1)];
+    g2l_r[i] = a.g2l ? v : e;
+  }
+  int my_id;
+  uint32_t my_key;
+  topk_lanes<4, kSelMaxRanges>(a.z, a.S, a.bias, 1, E, k, 0, cand, my_id, my_key);
+  // local id of lane j's expert: lane id_j % 64 holds it in slot id_j / 64
+  const int src = my_id < 0 ? 0 : my_id % kWave;
+  int le = -1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = __shfl(g2l_r[i], src, kWave);
+    if (my_id >= 0 && my_id / kWave == i) le = v;
+  }
+  const bool owned = lane < k && le >= 0 && le < a.E_local;
+  const uint64_t om = __ballot(owned);
+  int rank = 0, trank = 0;
+  for (int j = 0; j < k; ++j) {
+    const int idj = __builtin_amdgcn_readlane(my_id, j);
+    const bool below = idj < my_id;
+    rank += below ? 1 : 0;
+    trank += below && ((om >> j) & 1) ? 1 : 0;
+  }
+  const int n_tiles = min((int)__popcll(om), a.max_tiles);
+  const uint64_t hit = __ballot(owned && trank == want);
+  if (hit) {
+    const int sl = __builtin_ctzll(hit);
+    tl = make_int4(__builtin_amdgcn_readlane(le, sl), __builtin_amdgcn_readlane(rank, sl), 1,
+                   __builtin_amdgcn_readlane(my_id, sl));
+    tk = make_int4(0, 0, 0, 0);
+  }
+  if (writer && wave == 0) {
+    topk_store(k, 0, my_id, my_key, a.ids, a.w);
+    if (lane < k) a.slot_list[rank] = lane;
+    if (owned && trank < a.max_tiles) {
+      a.tiles[trank] = make_int4(le, rank, 1, my_id);
+      a.tile_tok[trank] = make_int4(0, 0, 0, 0);
+    }
+    if (lane == 0) *a.n_tiles = n_tiles;
+    // every expert's count (its slots) and offset (the slots of smaller ids); offsets[E] = k
+    for (int e = lane; e <= E; e += kWave) {
+      int c = 0, o = 0;
+      for (int j = 0; j < k; ++j) {
+        const int idj = __builtin_amdgcn_readlane(my_id, j);
+        c += idj == e ? 1 : 0;
+        o += idj < e ? 1 : 0;
+      }
+      if (e < E) a.counts[e] = c;
+      a.offsets[e] = o;
+    }
+  }
+  return n_tiles;
 }
 
 }  // namespace moe

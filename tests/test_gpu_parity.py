@@ -299,6 +299,26 @@ def test_layer_call_equals_the_four_calls(torch, cfg, T):
         assert np.array_equal(a, b), f"{name} differs between the layer call and the four calls"
 
 
+@pytest.mark.parametrize("E,k", [(8, 8), (40, 2), (100, 8), (256, 1), (256, 8), (256, 9), (300, 8), (1024, 8)])
+def test_topk_ties_against_a_stable_sort(torch, E, k):
+    """Top-k where most choices cross a tie: router bytes of zero (scale 0) make every logit equal
+    to its bias, drawn from four values.  The layer call (selection inside the gate/up launch up to
+    256 experts, in the front launch above) and the four calls must both give the k largest with
+    ties to the lower index, i.e. a stable sort of (-bias, index), and the normalised sigmoids."""
+    T = 3
+    _say(f"top-k ties: E={E}, k={k}")
+    wl = synth.make(synth.custom(T, 256, E, 64, k, name=f"ties_E{E}_k{k}"))
+    wl.router[:] = 0
+    rng = np.random.default_rng(1000 * E + k)
+    wl.bias = rng.choice(np.array([-0.5, 0.0, 0.25, 1.0], np.float32), size=E)
+    order = np.lexsort((np.arange(E), -wl.bias.astype(np.float64)))[:k]
+    sg = 1.0 / (1.0 + np.exp(-wl.bias[order].astype(np.float64)))
+    calls, fused = _run_both(make_layer(wl), wl, torch)
+    for got in (calls, fused):
+        assert np.array_equal(got[0].reshape(T, k), np.tile(order, (T, 1))), f"ids, E={E}, k={k}"
+        assert_close(got[1].reshape(T, k), np.tile(sg / sg.sum(), (T, 1)), what=f"weights E={E} k={k}")
+
+
 @pytest.mark.parametrize("k", [1, 5, 8, 9, 17])
 def test_combine_alone(torch, k):
     """moe_combine by itself, with and without an owner table (some experts unowned, one id past the
