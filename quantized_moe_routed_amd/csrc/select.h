@@ -117,11 +117,12 @@ __device__ __forceinline__ void logit_keys_upto(const float* __restrict__ z, int
   }
 }
 
-// Top-k (k <= kThrMaxK) of one wave's keys by a threshold: tau is the smallest of the row maxima
-// (rows of 16 lanes, per key slot) over the rows that hold a live expert, 0 when fewer than k rows
-// do.  Every such row's maximum is at least tau, so at least k live experts have a key >= tau;
-// those candidates go to LDS as composites (key, complement of the expert index), which are all
-// distinct, and a candidate's rank is the number of larger composites.  The k of rank < k, in rank
+// Top-k (k <= kThrMaxK) of one wave's keys by a threshold.  The row maxima (rows of 16 lanes, per
+// key slot; 0 for a row without a live expert) go one per lane, and tau is the largest of them that
+// at least k row maxima reach (0 when none does).  At least k distinct live experts then have a key
+// >= tau, so the k-th largest key is >= tau and every expert of the top k is a candidate.  The
+// candidates go to LDS as composites (key, complement of the expert index), which are all
+// distinct, and a candidate's rank is the number of larger composites; the k of rank < k, in rank
 // order, are exactly the k largest keys with ties to the lower index.  cand holds E + kThrMaxK
 // entries.  Lanes j < k receive slot j's expert and key.
 constexpr int kThrMaxK = 8;
@@ -139,21 +140,20 @@ template <int EPL>
 __device__ __forceinline__ void topk_threshold(const uint32_t (&key)[EPL], const bool (&live)[EPL], int E, int k,
                                                int lane, uint64_t* __restrict__ cand, int& my_id,
                                                uint32_t& my_key) {
-  uint32_t gm[EPL];
+  static_assert(EPL <= 16, "one row maximum per lane");
+  // lane 16 r + i (i < EPL): the maximum of row r of key slot i (keys of experts past E are 0)
+  uint32_t rm = 0;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) gm[i] = row_max_u32(key[i]);   // keys of experts past E are 0
-  uint32_t tau = 0xFFFFFFFFu;
-  int ng = 0;
+  for (int i = 0; i < EPL; ++i) {
+    const uint32_t g = row_max_u32(key[i]);
+    rm = (lane & 15) == i ? g : rm;
+  }
+  // how many row maxima reach this lane's; tau: the largest that at least k of them reach
+  int reach = 0;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (i * kWave + 16 * r < E) {
-        const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)gm[i], 16 * r);
-        tau = v < tau ? v : tau;
-        ++ng;
-      }
-  if (ng < k) tau = 0;
+  for (int q = 0; q < kWave; ++q)
+    if ((q & 15) < EPL) reach += (uint32_t)__builtin_amdgcn_readlane((int)rm, q) >= rm ? 1 : 0;
+  const uint32_t tau = wave_reduce_u32<true>((lane & 15) < EPL && reach >= k ? rm : 0u);
   int nc = 0;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
