@@ -42,9 +42,12 @@ constexpr int kStageRows = 4;     // slots per tile; their activation rows are s
 // and numbers the tiles itself from the logits (smallsel.h); one workgroup of an extra grid row
 // stores the routing results and the tile list for the later launches.
 // Bytes of the activation staging area (rows hi [+ lo], then a row of zeros), rounded to 16: the
-// one-token selection keeps its candidates past it.
+// one-token selection keeps its candidates past it, and the one-slot reduction its sums past those.
 __host__ __device__ constexpr size_t sel_cand_offset(int stage_rows, int K, bool lo) {
   return ((size_t)stage_rows * K * 2 * (lo ? 2 : 1) + (size_t)K * 2 + 15) & ~(size_t)15;
+}
+__host__ __device__ constexpr size_t one_red_offset(bool sel, int stage_rows, int K, bool lo) {
+  return sel_cand_offset(stage_rows, K, lo) + (sel ? kSelScratchBytes : 0);
 }
 
 template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL>
@@ -257,7 +260,68 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
       mterm();
     }
   }
-  // partial sums of the four waves, added in wave order (the staging area is reused)
+  if constexpr (ONE) {
+    // One slot: its hi row is component 0 of lanes 0..15, its lo row component 0 of lanes 16..31.
+    // Each wave adds the two (hi + lo, the lo half reaching lane l from lane l + 16) and leaves
+    // the sums past the staging area; after one barrier wave 0 adds the waves in order (the same
+    // additions as the general reduction below) and finishes the tile, lane 16 nt + l holding
+    // column 16 nt + l.
+    float* red1 = reinterpret_cast<float*>(smem + one_red_offset(SEL, a.stage_rows, K, LO));   // [wave][nt][mt][16]
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt) {
+        const float hi = acc[nt][mt][0];
+        const float lo = __shfl_xor(hi, 16, kWave);
+        if (lane < 16) red1[((wave * kNT + nt) * NM + mt) * 16 + lane] = hi + lo;
+      }
+    __syncthreads();
+    if (wave != 0 || lane >= 16 * kNT) return;
+    const int nt = lane >> 4, l = lane & 15;
+    auto R1 = [&](int w, int mt) { return red1[((w * kNT + nt) * NM + mt) * 16 + l]; };
+    if constexpr (MODE == MODE_DOWN) {
+      float v = R1(0, 0);
+#pragma unroll
+      for (int w = 1; w < kFfnWaves; ++w) v += R1(w, 0);
+      const int64_t slot = a.slot_list[p0];
+      a.y[slot * a.N + n0 + 16 * nt + l] = v * (1.0f / kSigmaH);
+    } else {
+      float gs = R1(0, 0), us = R1(0, 1);
+#pragma unroll
+      for (int w = 1; w < kFfnWaves; ++w) {
+        gs += R1(w, 0);
+        us += R1(w, 1);
+      }
+      const float inv = 1.0f / s_sig[0];   // a power of two: exact
+      const float h = silu(gs * inv) * (us * inv);
+      const int col = n0 + lane;
+      const int blk = col >> 5, kk = col & 31, gg = kk >> 3;
+      uint32_t hi, lo;
+      split_f16(h, hi, lo);   // h * kSigmaH * 2^6
+      const int64_t at = (int64_t)p0 * a.I + 32 * blk + 8 * gg + frag_val(kk & 7);
+      a.h_hi[at] = (uint16_t)hi;
+      a.h_lo[at] = (uint16_t)lo;
+      // block sum of h over the tile's 32 columns, in index order
+      float sacc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16 * kNT; ++i) sacc += __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(h), i));
+      if (lane == 0) {
+        split_f16(sacc * kSigmaH, hi, lo);
+        const int64_t at_s = (int64_t)p0 * a.nb32I + n0 / 32;
+        a.hs_hi[at_s] = (uint16_t)hi;
+        a.hs_lo[at_s] = (uint16_t)lo;
+      }
+      if (blockIdx.x == 0) {
+        const int nbI = a.I / 32;
+        for (int bb = nbI + lane; bb < a.nb32I; bb += 16 * kNT) {
+          a.hs_hi[(int64_t)p0 * a.nb32I + bb] = 0;
+          a.hs_lo[(int64_t)p0 * a.nb32I + bb] = 0;
+        }
+      }
+    }
+    return;
+  }
+  // partial sums of the waves, added in wave order (the staging area is reused)
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);   // [wave][nt][mt][r][lane]
   auto R = [&](int w, int nt, int mt, int r, int l) -> float& {
@@ -342,9 +406,10 @@ static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_
   const size_t stage = (size_t)t.stage_rows * t.K * 2 * (LO ? 2 : 1) + (size_t)t.K * 2;
   const size_t red = (size_t)kFfnWaves * kNT * NM * 4 * kWave * 4 + 16 * 33 * 4;
   size_t lds = stage > red ? stage : red;
-  if (SEL) {
-    const size_t sel = ONE ? sel_cand_offset(t.stage_rows, t.K, LO) + kSelScratchBytes : kSelScratchBytes;
-    if (lds < sel) lds = sel;
+  if (SEL && lds < kSelScratchBytes) lds = kSelScratchBytes;
+  if (ONE) {   // selection candidates (with SEL) and the one-slot sums past the staging area
+    const size_t one = one_red_offset(SEL, t.stage_rows, t.K, LO) + (size_t)kFfnWaves * kNT * NM * 16 * 4;
+    if (lds < one) lds = one;
   }
   auto kern = ffn_small_kernel<F, NM, LO, MODE, ONE, SEL>;
   if (lds > 64 * 1024) {

@@ -151,13 +151,16 @@ __device__ __forceinline__ int one_token_select(const SelArgs& a, bool writer, i
   int my_id;
   uint32_t my_key;
   topk_lanes<4, kSelMaxRanges>(a.z, a.S, a.bias, 1, E, k, 0, cand, my_id, my_key);
-  // local id of lane j's expert: lane id_j % 64 holds it in slot id_j / 64
-  const int src = my_id < 0 ? 0 : my_id % kWave;
-  int le = -1;
+  // local id of lane j's expert: lane id_j % 64 holds it in slot id_j / 64 (without a table it is id_j)
+  int le = my_id;
+  if (a.g2l) {
+    const int src = my_id < 0 ? 0 : my_id % kWave;
+    le = -1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = __shfl(g2l_r[i], src, kWave);
-    if (my_id >= 0 && my_id / kWave == i) le = v;
+    for (int i = 0; i < 4; ++i) {
+      const int v = __shfl(g2l_r[i], src, kWave);
+      if (my_id >= 0 && my_id / kWave == i) le = v;
+    }
   }
   const bool owned = lane < k && le >= 0 && le < a.E_local;
   const uint64_t om = __ballot(owned);
