@@ -106,7 +106,6 @@ size_t route_ws_bytes(int T, int E, int H, int fmt = MOE_W_Q8_0) { return align_
 // activation operand (hi plane; lo plane for fp32 activations) with its block
 // sums, and the intermediate h (hi, lo) with its block sums.  Block-sum rows
 // are padded to a multiple of 32 blocks.
-constexpr int kSmallTile = 4;     // slots per small tile of the expert kernels
 constexpr int kLargeTile = 128;   // slots per large tile
 constexpr int kLargeMin = 16;     // experts with at least this many slots use large tiles
 
@@ -114,15 +113,16 @@ int64_t max_tiles(int64_t slots, int64_t experts, int bm) { return (slots + bm -
 
 // Tile-list bounds for T tokens (an expert receives at most T slots).
 struct TilePlan {
-  int large_min, max_small, max_large;
+  int large_min, bm_small, max_small, max_large;
 };
 
-TilePlan tile_plan(int T, int H, int I, int k, int E_local) {
+TilePlan tile_plan(int T, int H, int I, int k, int E_local, int xt) {
   const int64_t slots = (int64_t)T * k;
   TilePlan p{};
   const bool large = T >= kLargeMin;
   p.large_min = large ? kLargeMin : 0x7FFFFFFF;
-  p.max_small = (int)max_tiles(slots, std::min<int64_t>(E_local, slots), kSmallTile);
+  p.bm_small = moe::small_tile_rows(H, I, xt == MOE_ACT_F32);
+  p.max_small = (int)max_tiles(slots, std::min<int64_t>(E_local, slots), p.bm_small);
   p.max_large = large ? (int)max_tiles(slots, std::min<int64_t>(E_local, slots / kLargeMin), kLargeTile) : 0;
   return p;
 }
@@ -137,7 +137,7 @@ FwdLayout fwd_layout(int T, int H, int I, int k, int E_local, int xt) {
   FwdLayout L{};
   const size_t TK = (size_t)T * k;
   const size_t nb32H = pad32(H / 32), nb32I = pad32(I / 32);
-  const TilePlan tp = tile_plan(T, H, I, k, E_local);
+  const TilePlan tp = tile_plan(T, H, I, k, E_local, xt);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -147,7 +147,7 @@ FwdLayout fwd_layout(int T, int H, int I, int k, int E_local, int xt) {
   L.n_small = take(sizeof(int32_t));
   L.n_large = take(sizeof(int32_t));
   L.small = take((size_t)tp.max_small * 4 * sizeof(int32_t));
-  L.small_tok = take((size_t)tp.max_small * 4 * sizeof(int32_t));
+  L.small_tok = take((size_t)tp.max_small * moe::kSmallRowsMax * sizeof(int32_t));
   L.large = take((size_t)tp.max_large * 4 * sizeof(int32_t));
   L.sigma = take((size_t)T * sizeof(float));
   L.xq_hi = take((size_t)T * H * 2);
@@ -365,7 +365,7 @@ moe_status forward_setup(const char* fn, const void* x, int32_t xt, int32_t T, i
   auto at16 = [&](size_t o) { return reinterpret_cast<uint16_t*>(wsb + o); };
   moe::FfnArgs& a = f.a;
   a = moe::FfnArgs{};
-  const TilePlan tp = tile_plan(T, H, I, k, E_local);
+  const TilePlan tp = tile_plan(T, H, I, k, E_local, xt);
   a.T = T; a.H = H; a.I = I; a.k = k;
   a.fg = local->gate.fmt;
   a.fd = local->down.fmt;
@@ -381,6 +381,7 @@ moe_status forward_setup(const char* fn, const void* x, int32_t xt, int32_t T, i
   a.n_small = reinterpret_cast<const int32_t*>(wsb + L.n_small);
   a.n_large = reinterpret_cast<const int32_t*>(wsb + L.n_large);
   a.max_small = tp.max_small;
+  a.bm_small = tp.bm_small;
   a.max_large = tp.max_large;
   a.xq_hi = at16(L.xq_hi);
   a.xq_lo = xt == MOE_ACT_F32 ? at16(L.xq_lo) : nullptr;
@@ -401,7 +402,7 @@ moe_status forward_setup(const char* fn, const void* x, int32_t xt, int32_t T, i
   tl.E_local = E_local;
   tl.n_slots = T * k;
   tl.large_min = tp.large_min;
-  tl.bm_small = kSmallTile;
+  tl.bm_small = tp.bm_small;
   tl.max_small = tp.max_small;
   tl.bm_large = kLargeTile;
   tl.max_large = tp.max_large;
@@ -537,6 +538,7 @@ moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, in
     sel.E_local = E_local;
     sel.g2l = g2l;
     sel.max_tiles = f.tl.max_small;
+    sel.bm = f.tl.bm_small;
     sel.ids = ids;
     sel.w = w;
     sel.counts = counts;

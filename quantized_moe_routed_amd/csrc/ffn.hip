@@ -34,7 +34,7 @@ namespace moe {
 constexpr int kFfnThreads = 512;
 constexpr int kFfnWaves = kFfnThreads / 64;
 constexpr int kNT = 2;            // 16-column output tiles per workgroup
-constexpr int kStageRows = 4;     // slots per tile; their activation rows are staged in LDS
+constexpr int kStageRows = kSmallRowsMax;   // slots per tile at most; their activation rows are staged in LDS
 
 // ONE: every tile holds a single slot (one token in the batch), so only the
 // first component of each output fragment is ever needed.
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   __shared__ float s_sig[16];
 
   const int tile = blockIdx.y;
-  int4 tl, tk;
+  int4 tl, tk0, tk1;   // the tile; the operand rows of its slots 0..3 and 4..7
   if constexpr (SEL) {
     // the grid's last row holds no tile: its workgroup 0 stores the routing results
     const bool writer = blockIdx.y == gridDim.y - 1;
@@ -69,24 +69,36 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
       static_assert(kFfnWaves <= kSelMaxTokens, "one candidate area per wave");
       uint64_t* cand = reinterpret_cast<uint64_t*>(smem + sel_cand_offset(a.stage_rows, a.K, LO)) +
                        (size_t)(threadIdx.x / kWave) * (a.sel.E + kThrMaxK);
-      tl = tk = make_int4(0, 0, 0, 0);
-      const int n = one_token_select(a.sel, writer, writer ? -1 : tile, cand, tl, tk);
+      tl = tk0 = tk1 = make_int4(0, 0, 0, 0);
+      const int n = one_token_select(a.sel, writer, writer ? -1 : tile, cand, tl);
       if (writer || tile >= n) return;
     } else {
       __shared__ SelLds sl;
       small_select<kFfnThreads>(a.sel, sl, writer, writer ? -1 : tile, reinterpret_cast<uint64_t*>(smem));
       if (writer || tile >= sl.n_tiles) return;
       tl = sl.tile;
-      tk = sl.tok;
+      tk0 = sl.tok[0];
+      tk1 = sl.tok[1];
     }
   } else {
     if (tile >= *a.n_tiles) return;
     tl = a.tiles[tile];
     // operand rows of the tile: tokens (gate/up, listed with the tile) or grouped positions (down)
-    tk = MODE == MODE_GATEUP ? a.tile_tok[tile] : make_int4(tl.y, tl.y + 1, tl.y + 2, tl.y + 3);
+    if constexpr (MODE == MODE_GATEUP) {
+      tk0 = a.tile_tok[2 * tile];
+      tk1 = a.tile_tok[2 * tile + 1];
+    } else {
+      tk0 = make_int4(tl.y, tl.y + 1, tl.y + 2, tl.y + 3);
+      tk1 = make_int4(tl.y + 4, tl.y + 5, tl.y + 6, tl.y + 7);
+    }
   }
   const int le = tl.x, p0 = tl.y, rows = tl.z;
-  auto row_of = [&](int m) { return m == 0 ? tk.x : m == 1 ? tk.y : m == 2 ? tk.z : tk.w; };
+  auto row_of = [&](int m) {
+    const int j = m & 3;
+    const int a0 = j == 0 ? tk0.x : j == 1 ? tk0.y : j == 2 ? tk0.z : tk0.w;
+    const int a1 = j == 0 ? tk1.x : j == 1 ? tk1.y : j == 2 ? tk1.z : tk1.w;
+    return m < 4 ? a0 : a1;
+  };
   const int n0 = blockIdx.x * 16 * kNT;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int c16 = lane & 15, g = lane >> 4;
@@ -177,14 +189,14 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   };
   if constexpr (Codes<F>::kHasM) load_m(u_beg);
 
-  // A fragment rows: 0..3 the hi plane of slots 0..3, 4..7 their lo plane, 8..15 zero
-  const int slot_m = c16 & 3;
-  const bool mvalid = slot_m < rows && (c16 < 4 || (LO && c16 < 8));
+  // A fragment rows: 0..7 the hi plane of slots 0..7, 8..15 their lo plane (zero without one)
+  const int slot_m = c16 & 7;
+  const bool mvalid = slot_m < rows && (c16 < 8 || LO);
   const int arow = row_of(slot_m < rows ? slot_m : 0);
-  const uint16_t* pa = (mvalid ? (c16 < 4 ? st_hi : st_lo) + slot_m * K : st_zero) + 8 * g;
-  // the m-term operand: rows 0..3 hi, 4..7 lo of the block sums
-  const bool svalid = slot_m < rows && c16 < 8;
-  const uint16_t* ps = (c16 < 4 ? a.s_hi : a.s_lo) + (int64_t)arow * a.nb32;
+  const uint16_t* pa = (mvalid ? (c16 < 8 ? st_hi : st_lo) + slot_m * K : st_zero) + 8 * g;
+  // the m-term operand: rows 0..7 hi, 8..15 lo of the block sums
+  const bool svalid = slot_m < rows;
+  const uint16_t* ps = (c16 < 8 ? a.s_hi : a.s_lo) + (int64_t)arow * a.nb32;
   // m-term operands of a group of up to 4 of this wave's units (lane group g: unit ug + g): the m
   // values of the lane's column and the block sums of the slots (rows 0..3 hi, 4..7 lo)
   uint4 sv = zero;
@@ -261,8 +273,8 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
     }
   }
   if constexpr (ONE) {
-    // One slot: its hi row is component 0 of lanes 0..15, its lo row component 0 of lanes 16..31.
-    // Each wave adds the two (hi + lo, the lo half reaching lane l from lane l + 16) and leaves
+    // One slot: its hi row is component 0 of lanes 0..15, its lo row component 0 of lanes 32..47.
+    // Each wave adds the two (hi + lo, the lo half reaching lane l from lane l + 32) and leaves
     // the sums past the staging area; after one barrier wave 0 adds the waves in order (the same
     // additions as the general reduction below) and finishes the tile, lane 16 nt + l holding
     // column 16 nt + l.
@@ -272,7 +284,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
 #pragma unroll
       for (int mt = 0; mt < NM; ++mt) {
         const float hi = acc[nt][mt][0];
-        const float lo = __shfl_xor(hi, 16, kWave);
+        const float lo = __shfl_xor(hi, 32, kWave);
         if (lane < 16) red1[((wave * kNT + nt) * NM + mt) * 16 + lane] = hi + lo;
       }
     __syncthreads();
@@ -334,31 +346,33 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
 #pragma unroll
       for (int r = 0; r < 4; ++r) R(wave, nt, mt, r, lane) = acc[nt][mt][r];
   __syncthreads();
-  // thread t < 64 owns output (slot m, column l) of each 16-column tile: the sum over the waves
-  // of the hi row (lane l, component m) and the lo row (lane l+16, component m)
+  // thread t < 128 owns output (slot m, column l) of each 16-column tile: the sum over the waves of
+  // the hi row m (lane 16 (m / 4) + l, component m % 4) and the lo row 8 + m (lane
+  // 16 (2 + m / 4) + l, the same component)
   const int m = tid >> 4, l = tid & 15;
-  const bool owner = tid < 64;
+  const bool owner = tid < 16 * kStageRows;
+  const int lhi = 16 * ((m >> 2) & 1) + l, llo = lhi + 32, cm = m & 3;
   if constexpr (MODE == MODE_DOWN) {
     if (owner && m < rows) {
       const int64_t slot = a.slot_list[p0 + m];
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
-        float v = R(0, nt, 0, m, l) + R(0, nt, 0, m, l + 16);
+        float v = R(0, nt, 0, cm, lhi) + R(0, nt, 0, cm, llo);
 #pragma unroll
-        for (int w = 1; w < kFfnWaves; ++w) v += R(w, nt, 0, m, l) + R(w, nt, 0, m, l + 16);
+        for (int w = 1; w < kFfnWaves; ++w) v += R(w, nt, 0, cm, lhi) + R(w, nt, 0, cm, llo);
         a.y[slot * a.N + n0 + 16 * nt + l] = v * (1.0f / kSigmaH);
       }
     }
   } else {
-    float* hbuf = red + kFfnWaves * kNT * NM * 4 * kWave;   // [4][33]
-    const float inv = 1.0f / s_sig[m & 3];                   // a power of two: exact
+    float* hbuf = red + kFfnWaves * kNT * NM * 4 * kWave;   // [8][33]
+    const float inv = 1.0f / s_sig[m & 7];                   // a power of two: exact
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-      float gs = R(0, nt, 0, m, l) + R(0, nt, 0, m, l + 16), us = R(0, nt, 1, m, l) + R(0, nt, 1, m, l + 16);
+      float gs = R(0, nt, 0, cm, lhi) + R(0, nt, 0, cm, llo), us = R(0, nt, 1, cm, lhi) + R(0, nt, 1, cm, llo);
 #pragma unroll
       for (int w = 1; w < kFfnWaves; ++w) {
-        gs += R(w, nt, 0, m, l) + R(w, nt, 0, m, l + 16);
-        us += R(w, nt, 1, m, l) + R(w, nt, 1, m, l + 16);
+        gs += R(w, nt, 0, cm, lhi) + R(w, nt, 0, cm, llo);
+        us += R(w, nt, 1, cm, lhi) + R(w, nt, 1, cm, llo);
       }
       const int cl = 16 * nt + l;
       float h = 0.0f;
@@ -404,7 +418,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
 template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL = false>
 static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_t s) {
   const size_t stage = (size_t)t.stage_rows * t.K * 2 * (LO ? 2 : 1) + (size_t)t.K * 2;
-  const size_t red = (size_t)kFfnWaves * kNT * NM * 4 * kWave * 4 + 16 * 33 * 4;
+  const size_t red = (size_t)kFfnWaves * kNT * NM * 4 * kWave * 4 + kStageRows * 33 * 4;
   size_t lds = stage > red ? stage : red;
   if (SEL && lds < kSelScratchBytes) lds = kSelScratchBytes;
   if (ONE) {   // selection candidates (with SEL) and the one-slot sums past the staging area
@@ -421,12 +435,19 @@ static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_
   return hipGetLastError();
 }
 
+int small_tile_rows(int H, int I, bool f32_act) {
+  // (the staging area of 8 rows; the reduction area and the selection's LDS are smaller)
+  auto stage = [](int K, bool lo) { return (size_t)kSmallRowsMax * K * 2 * (lo ? 2 : 1) + (size_t)K * 2; };
+  constexpr size_t kTwoPerCu = 72 * 1024;
+  return stage(H, f32_act) <= kTwoPerCu && stage(I, true) <= kTwoPerCu ? kSmallRowsMax : 4;
+}
+
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   hipError_t err = hipSuccess;
   FfnTileArgs t{};
   t.slot_list = a.slot_list;
   t.k = a.k;
-  t.stage_rows = a.T < kStageRows ? a.T : kStageRows;
+  t.stage_rows = a.T < a.bm_small ? a.T : a.bm_small;
   t.kc = frag_consts();
   // gate/up: activations (hi [+ lo]) x gate, up  ->  h
   t.a_hi = a.xq_hi; t.a_lo = a.xq_lo; t.s_hi = a.sq_hi; t.s_lo = a.sq_lo; t.sigma = a.sigma;

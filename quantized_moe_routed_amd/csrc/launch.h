@@ -45,7 +45,7 @@ struct TileLists {
   int bm_small, max_small, bm_large, max_large;
   int4 *small, *large;
   int32_t *n_small, *n_large;
-  int4* small_tok;              // tokens of the rows of each small tile (bm_small <= 4)
+  int4* small_tok;              // tokens of the rows of each small tile: two int4 per tile (bm_small <= 8)
   const int32_t* slot_list;
   int k;
 };
@@ -68,6 +68,7 @@ struct FfnArgs {
   const int4* small_tok;
   const int32_t *n_small, *n_large;
   int max_small, max_large;   // max_large = 0: no large tiles can exist
+  int bm_small;               // slots per small tile (4 or 8)
   const uint16_t *xq_hi, *xq_lo, *sq_hi, *sq_lo;
   const float* sigma;
   uint16_t *h_hi, *h_lo, *hs_hi, *hs_lo;
@@ -82,9 +83,15 @@ struct FfnArgs {
 hipError_t launch_prep(const void* x, int act, int fmt, int T, int H, int nb32, uint16_t* xq_hi, uint16_t* xq_lo,
                        uint16_t* sq_hi, uint16_t* sq_lo, float* sigma, const TileLists& tl, hipStream_t s);
 
-// gate/up then down: small tiles (up to 4 slots, 32 output columns per
+// gate/up then down: small tiles (up to 8 slots, 32 output columns per
 // workgroup) and large tiles (up to 128 slots, 64 columns per workgroup).
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+
+// Slots per small tile: 8 when the activation rows of 8 slots stay within the LDS that lets two
+// workgroups share a compute unit, for gate/up (K = H; hi and lo planes for fp32 activations) and
+// for down (K = I, hi and lo planes), else 4.
+constexpr int kSmallRowsMax = 8;
+int small_tile_rows(int H, int I, bool f32_act);
 
 hipError_t launch_combine(const float* y, const float* w, const int32_t* ids, const int32_t* g2l, int T, int k,
                           int H, int E, float* out, hipStream_t s);

@@ -46,11 +46,12 @@ __device__ void build_tiles(const int32_t* __restrict__ counts, const int32_t* _
   for (int i = 0; i < mt && base + i < max_tiles; ++i) {
     const int rows = min(bm, n - bm * i);
     tiles[base + i] = make_int4(l, p + bm * i, rows, tid);
-    if (tok) {
-      int r[4];
+    if (tok) {   // (bm <= kSmallRowsMax)
+      int r[kSmallRowsMax];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r[j] = j < rows ? slot_list[p + bm * i + j] / k : 0;
-      tok[base + i] = make_int4(r[0], r[1], r[2], r[3]);
+      for (int j = 0; j < kSmallRowsMax; ++j) r[j] = j < rows ? slot_list[p + bm * i + j] / k : 0;
+      tok[2 * (base + i)] = make_int4(r[0], r[1], r[2], r[3]);
+      tok[2 * (base + i) + 1] = make_int4(r[4], r[5], r[6], r[7]);
     }
   }
   if (tid == 0) {

@@ -11,13 +11,13 @@
 // id, capped at max_tiles.
 #pragma once
 #include "device.h"
+#include "launch.h"
 #include "select.h"
 
 namespace moe {
 
 constexpr int kSelMaxTokens = 8;
 constexpr int kSelMaxE = 256;    // experts: 4 per lane of a wave
-constexpr int kSelTile = 4;       // slots per small tile
 
 struct SelArgs {
   const float* z;                // [S][T][E] partial logits over aligned block ranges ([T][E] finished ones if S == 0)
@@ -25,7 +25,7 @@ struct SelArgs {
   const float* bias;
   int T, E, k, E_local;
   const int32_t* g2l;            // NULL: every expert owned, local = global
-  int max_tiles;
+  int max_tiles, bm;             // small tiles: at most max_tiles of at most bm slots
   int32_t *ids, *counts, *offsets, *slot_list, *n_tiles;
   float* w;
   int4 *tiles, *tile_tok;
@@ -36,14 +36,14 @@ struct SelLds {
   int32_t slot[kSelMaxTokens * 32];
   int32_t cnt[kSelMaxE], off[kSelMaxE + 1], g2l[kSelMaxE];
   int32_t wave_tot[16];
-  int4 tile, tok;
+  int4 tile, tok[2];
   int32_t n_tiles;
 };
 
 // LDS for the threshold selection: E + kThrMaxK candidates per token
 constexpr size_t kSelScratchBytes = (size_t)kSelMaxTokens * (kSelMaxE + kThrMaxK) * sizeof(uint64_t);
 
-// want: the tile whose description lands in L.tile / L.tok (when want < L.n_tiles).  scratch:
+// want: the tile whose description lands in L.tile / L.tok[2] (when want < L.n_tiles).  scratch:
 // kSelScratchBytes of LDS, free again when the call returns.
 template <int NT>
 __device__ __forceinline__ void small_select(const SelArgs& a, SelLds& L, bool writer, int want,
@@ -83,7 +83,8 @@ __device__ __forceinline__ void small_select(const SelArgs& a, SelLds& L, bool w
   }
   // tiles of up to 4 slots per owned expert that received slots, numbered in ascending id
   const int le = tid < E ? g2l_e : -1;
-  const int mt = (c > 0 && le >= 0 && le < a.E_local) ? (c + kSelTile - 1) / kSelTile : 0;
+  const int bm = a.bm;
+  const int mt = (c > 0 && le >= 0 && le < a.E_local) ? (c + bm - 1) / bm : 0;
   int incl = mt;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
@@ -103,18 +104,21 @@ __device__ __forceinline__ void small_select(const SelArgs& a, SelLds& L, bool w
   for (int i = 0; i < mt; ++i) {
     const int ti = base + i;
     if (ti >= a.max_tiles) break;
-    const int rows = min(kSelTile, c - kSelTile * i), p0 = o + kSelTile * i;
-    int r[kSelTile];
+    const int rows = min(bm, c - bm * i), p0 = o + bm * i;
+    int r[kSmallRowsMax];
 #pragma unroll
-    for (int j = 0; j < kSelTile; ++j) r[j] = j < rows ? L.slot[p0 + j] / k : 0;
-    const int4 tl = make_int4(le, p0, rows, tid), tk = make_int4(r[0], r[1], r[2], r[3]);
+    for (int j = 0; j < kSmallRowsMax; ++j) r[j] = j < rows ? L.slot[p0 + j] / k : 0;
+    const int4 tl = make_int4(le, p0, rows, tid), tk0 = make_int4(r[0], r[1], r[2], r[3]),
+               tk1 = make_int4(r[4], r[5], r[6], r[7]);
     if (ti == want) {
       L.tile = tl;
-      L.tok = tk;
+      L.tok[0] = tk0;
+      L.tok[1] = tk1;
     }
     if (writer) {
       a.tiles[ti] = tl;
-      a.tile_tok[ti] = tk;
+      a.tile_tok[2 * ti] = tk0;
+      a.tile_tok[2 * ti + 1] = tk1;
     }
   }
   if (writer) {
@@ -132,10 +136,10 @@ __device__ __forceinline__ void small_select(const SelArgs& a, SelLds& L, bool w
 // own E + kThrMaxK entries of LDS) and finds its workgroup's tile with no LDS exchange and no
 // barrier: slot j's position is the number of selected ids below id_j, its tile number the number
 // of owned selected ids below id_j (tiles in ascending expert id, as in small_select).  Wave 0 of
-// the writer stores what small_select stores for one token.  Returns the tile count; tl / tk
-// receive tile want when want is below it.
+// the writer stores what small_select stores for one token.  Returns the tile count; tl receives
+// tile want when want is below it (its one row is token 0).
 __device__ __forceinline__ int one_token_select(const SelArgs& a, bool writer, int want, uint64_t* cand,
-                                                int4& tl, int4& tk) {
+                                                int4& tl) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int E = a.E, k = a.k;
   // ownership table in registers, fetched ahead of the selection: expert i * 64 + lane in slot i
@@ -177,14 +181,14 @@ __device__ __forceinline__ int one_token_select(const SelArgs& a, bool writer, i
     const int sl = __builtin_ctzll(hit);
     tl = make_int4(__builtin_amdgcn_readlane(le, sl), __builtin_amdgcn_readlane(rank, sl), 1,
                    __builtin_amdgcn_readlane(my_id, sl));
-    tk = make_int4(0, 0, 0, 0);
   }
   if (writer && wave == 0) {
     topk_store(k, 0, my_id, my_key, a.ids, a.w);
     if (lane < k) a.slot_list[rank] = lane;
     if (owned && trank < a.max_tiles) {
       a.tiles[trank] = make_int4(le, rank, 1, my_id);
-      a.tile_tok[trank] = make_int4(0, 0, 0, 0);
+      a.tile_tok[2 * trank] = make_int4(0, 0, 0, 0);
+      a.tile_tok[2 * trank + 1] = make_int4(0, 0, 0, 0);
     }
     if (lane == 0) *a.n_tiles = n_tiles;
     // every expert's count (its slots) and offset (the slots of smaller ids); offsets[E] = k
