@@ -251,8 +251,10 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
           for (int mt = 0; mt < NM; ++mt) p[mt] = mfma16(av, bf[mt], zero4);
 #pragma unroll
           for (int mt = 0; mt < NM; ++mt) {
-            const float d = d_of<F>(dw[j][nt][mt], i);
-            // output row 4(l/16)+r holds slot r (hi or lo plane) for the first two lane groups
+            float d = d_of<F>(dw[j][nt][mt], i);
+            // several slots: convert the scale once, then plain fp32 FMAs (one slot: a single
+            // mixed-precision FMA is cheaper)
+            if (!ONE) asm volatile("" : "+v"(d));
             acc[nt][mt][0] = fmaf(d, p[mt][0], acc[nt][mt][0]);
             if (!ONE) {
               acc[nt][mt][1] = fmaf(d, p[mt][1], acc[nt][mt][1]);

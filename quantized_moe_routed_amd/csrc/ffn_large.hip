@@ -300,6 +300,7 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
               bf[nt][mt][0] = Codes<F>::frag(cw[j][nt][mt][0], ib, a.kc);
               bf[nt][mt][1] = Codes<F>::frag(cw[j][nt][mt][1], ib, a.kc);
               d[nt][mt] = d_of<F>(dw[j][nt][mt], ib);
+              pin(d[nt][mt]);   // converted once: the 16 folds are plain fp32 FMAs, not mixed-precision ones
             }
           }
 #pragma unroll
