@@ -226,7 +226,8 @@ TRAFFIC_KERNELS = {
     "decode": ("ffn_gateup", "moe::ffn_small_kernel<2, 2, true, 0, true, true>",
                ["quantized_moe_routed_amd/csrc/ffn.hip", "quantized_moe_routed_amd/csrc/ffn.h",
                 "quantized_moe_routed_amd/csrc/fmt.h", "quantized_moe_routed_amd/csrc/device.h",
-                "quantized_moe_routed_amd/csrc/smallsel.h", "quantized_moe_routed_amd/csrc/select.h"]),
+                "quantized_moe_routed_amd/csrc/smallsel.h", "quantized_moe_routed_amd/csrc/select.h",
+                "quantized_moe_routed_amd/csrc/launch.h"]),
 }
 COPY_BYTES = 256 << 20   # the calibration copy: reads and writes this many bytes
 
