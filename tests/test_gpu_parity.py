@@ -353,19 +353,19 @@ def test_combine_alone(torch, k):
                 assert_close(got, ref, what=f"combine k={k}")
 
 
-@pytest.mark.parametrize("I", [2304, 4096])
-def test_layer_call_one_token_down_widths(torch, I):
-    """One token with 2-bit down weights at two expert widths: the down launch's waves take one or
-    two code units of each expert row; I=2304 (nine units) leaves waves with one unit and waves
-    with none."""
-    _say(f"layer call vs four calls: one token, I={I}")
-    wl = synth.make(synth.custom(1, 2048, 64, I, 8, gate_fmt=synth.FMT_Q2SM, up_fmt=synth.FMT_Q2SM,
-                                 down_fmt=synth.FMT_Q2SM, bias="zipf1.1", name=f"down_w{I}"))
+@pytest.mark.parametrize("I,k", [(2304, 8), (4096, 8), (1280, 8), (2048, 3)])
+def test_layer_call_one_token_down_widths(torch, I, k):
+    """One token with 2-bit down weights at several expert widths: the down launch's waves take one
+    code unit each up to I=2048 (I=1280: five units, three waves empty; k=3: three tiles) and one
+    or two beyond (I=2304, nine units: waves with one unit and waves with none)."""
+    _say(f"layer call vs four calls: one token, I={I}, k={k}")
+    wl = synth.make(synth.custom(1, 2048, 64, I, k, gate_fmt=synth.FMT_Q2SM, up_fmt=synth.FMT_Q2SM,
+                                 down_fmt=synth.FMT_Q2SM, bias="zipf1.1", name=f"down_w{I}_k{k}"))
     layer = make_layer(wl)
     calls, fused = _run_both(layer, wl, torch)
     for name, a, b in zip(("ids", "w", "counts", "offsets", "slot_list", "y_slot", "out"), calls, fused):
         assert np.array_equal(a, b), f"{name} differs between the layer call and the four calls"
-    check_against_oracle(wl, run(layer, wl, torch), oracle_expect(wl), what=f"one token I={I}")
+    check_against_oracle(wl, run(layer, wl, torch), oracle_expect(wl), what=f"one token I={I} k={k}")
 
 
 @pytest.mark.parametrize("T", [1, 5, 24])
