@@ -200,7 +200,7 @@ def measure(name, steps, warmup, torch):
     return wl, res
 
 
-def cpu_baseline(budget_s=15.0, max_tokens=400):
+def cpu_baseline(budget_s=15.0, max_tokens=1600):
     """The CPU oracle, as it stands, on a bounded sample of the decode workload."""
     import oracle
     import synth
