@@ -78,7 +78,7 @@ def input_pool(wl, n_batches, torch):
     return [xs[i * T:(i + 1) * T] for i in range(n_batches)], toks
 
 
-LARGE_MIN = 16   # experts with this many slots or more run on the large-tile kernel (batches of 16+ tokens)
+LARGE_MIN = 9    # experts with this many slots or more run on the large-tile kernel (batches of 9+ tokens)
 TRACE_EVERY = 8  # the kernel events of the timed region sample one launch in this many
 
 

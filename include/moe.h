@@ -42,8 +42,9 @@
  *    unmodified, and moe_last_error() describes the problem (thread-local).
  *  - T = 0 is a successful no-op.  There are no environment switches and no
  *    fallback paths: every expert runs on the fp16 matrix cores, on tiles of up
- *    to 4 slots, or of up to 128 slots for experts with 16 or more slots in a
- *    batch of 16 or more tokens.
+ *    to 8 slots (4 where the activation rows of 8 slots would not fit the LDS
+ *    of two workgroups per compute unit), or of up to 128 slots for experts with
+ *    9 or more slots in a batch of 9 or more tokens.
  *  - Calls that overlap on one stream are ordered; calls sharing a workspace
  *    on different streams race.
  */

@@ -107,7 +107,8 @@ size_t route_ws_bytes(int T, int E, int H, int fmt = MOE_W_Q8_0) { return align_
 // sums, and the intermediate h (hi, lo) with its block sums.  Block-sum rows
 // are padded to a multiple of 32 blocks.
 constexpr int kLargeTile = 128;   // slots per large tile
-constexpr int kLargeMin = 16;     // experts with at least this many slots use large tiles
+constexpr int kLargeMin = 9;      // experts with at least this many slots use large tiles (batches of 9+ tokens);
+                                  // fewer slots fit one small tile of 8
 
 int64_t max_tiles(int64_t slots, int64_t experts, int bm) { return (slots + bm - 1) / bm + experts; }
 
