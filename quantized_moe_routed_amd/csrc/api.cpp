@@ -556,8 +556,8 @@ moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, in
     const moe::PrepOut po{f.a.nb32H, const_cast<uint16_t*>(f.a.xq_hi), const_cast<uint16_t*>(f.a.xq_lo),
                           const_cast<uint16_t*>(f.a.sq_hi), const_cast<uint16_t*>(f.a.sq_lo),
                           const_cast<float*>(f.a.sigma)};
-    // the operands ride on the router's launch (batches this small take the one-expert-per-wave
-    // logits kernel)
+    // the operands ride on the router's launch (batches this small take the small-batch logits
+    // kernels)
     e = moe::launch_logits(x, xt, T, H, router->fmt, qm(*router), bias, ws, &S, s, &po);
     if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: logits launch");
     e = moe::launch_front(reinterpret_cast<const float*>(ws), S, bias, T, E, k, ids, w, counts, offsets, slot_list, x,

@@ -1,8 +1,8 @@
-// Expert FFN on fp16 matrix cores, for tiles of up to 4 routed slots of one
+// Expert FFN on fp16 matrix cores, for tiles of up to 8 routed slots of one
 // expert (decode-size batches, and every batch until the large-tile kernel
 // takes the heavy experts).
 //
-// A workgroup owns one tile (up to 4 slots of one expert) and 32 output
+// A workgroup owns one tile (up to 8 slots of one expert) and 32 output
 // columns; its 8 waves split the contraction: wave w takes a contiguous
 // range of the code units of the rows (a unit is 8 blocks of Q2SM or 2 blocks
 // of Q8_0: 64 bytes of codes per row) and the m-term chunks w, w+8, ... of 32
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   const bool svalid = slot_m < rows;
   const uint16_t* ps = (c16 < 8 ? a.s_hi : a.s_lo) + (int64_t)arow * a.nb32;
   // m-term operands of a group of up to 4 of this wave's units (lane group g: unit ug + g): the m
-  // values of the lane's column and the block sums of the slots (rows 0..3 hi, 4..7 lo)
+  // values of the lane's column and the block sums of the slots (rows 0..7 hi, 8..15 lo)
   uint4 sv = zero;
   auto load_s = [&](int ug) {
     const int u = ug + g;

@@ -15,9 +15,9 @@ constexpr int kPrepThreads = 1024;
 // received slots, in ascending global id: tile i covers grouped positions
 // p0 .. p0+rows-1 of local expert .x.  Tiles past max_tiles, and rows past the
 // n_slots grouped positions, are never produced, whatever the counts hold.
-// With tok != NULL (tiles of up to 4 slots), tok[i] also receives the token of each row of tile i
-// (slot / k; 0 for rows past the tile), so that the expert kernel can fetch the tile's activation
-// rows without first reading the slot list.
+// With tok != NULL (small tiles, bm <= kSmallRowsMax), tok[2 i] and tok[2 i + 1] also receive the
+// token of each row of tile i (slot / k; 0 for rows past the tile), so that the expert kernel can
+// fetch the tile's activation rows without first reading the slot list.
 __device__ void build_tiles(const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
                             const int32_t* __restrict__ g2l, int E, int E_local, int n_slots, int bm, int lo_n,
                             int hi_n, int max_tiles, int4* __restrict__ tiles, int32_t* __restrict__ n_tiles,

@@ -7,12 +7,17 @@
 //                    r_b = d_b * p            (Q8_0; an fp32 router has r_b = p)
 //   z = balanced pairwise sum over b: (r0 + r1), (r2 + r3), ... level by level,
 //       an odd last element carried up unchanged;  then z += bias.
-// A wave holds one expert row: lane l owns the C consecutive blocks
-// l*C .. l*C+C-1, adds them pairwise in registers (the first log2 C levels of
-// the tree) and the remaining levels are an xor butterfly across lanes, which
-// adds adjacent subtrees exactly as the tree does (IEEE addition commutes).
-// Lanes past the last block contribute +0.0: padding the tree with zeros
-// changes no value, so the result equals the carry-up tree for any block count.
+// Three layouts take these sums.  fp32 router: a wave holds one expert row,
+// lane l owns the C consecutive blocks l*C .. l*C+C-1, adds them pairwise in
+// registers (the first log2 C levels of the tree) and the remaining levels are
+// an xor butterfly across lanes, which adds adjacent subtrees exactly as the
+// tree does (IEEE addition commutes).  Q8_0 router, batches below 16 tokens: a
+// wave per 16 experts and four units, a workgroup per aligned range of 32
+// blocks.  Q8_0 router, 16+ tokens: a token per lane, a workgroup per aligned
+// range.  The last two write each range's subtree sum; the selection adds the
+// ranges pairwise (the tree's top levels) and then the bias.  Blocks past the
+// last contribute +0.0: padding the tree with zeros changes no value, so the
+// result equals the carry-up tree for any block count.
 #include <type_traits>
 
 #include "device.h"

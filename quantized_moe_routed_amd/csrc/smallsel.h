@@ -7,7 +7,7 @@
 // results (ids, weights, counts, offsets, slot list, tile list) for the later
 // launches.  The results equal those of the separate kernels: the same top-k
 // (select.h), the stable counting sort of the slots by expert, and tiles of up
-// to 4 slots over the owned experts that received slots, in ascending global
+// to bm slots over the owned experts that received slots, in ascending global
 // id, capped at max_tiles.
 #pragma once
 #include "device.h"
@@ -81,7 +81,7 @@ __device__ __forceinline__ void small_select(const SelArgs& a, SelLds& L, bool w
       L.slot[r] = tid;
     }
   }
-  // tiles of up to 4 slots per owned expert that received slots, numbered in ascending id
+  // tiles of up to bm slots per owned expert that received slots, numbered in ascending id
   const int le = tid < E ? g2l_e : -1;
   const int bm = a.bm;
   const int mt = (c > 0 && le >= 0 && le < a.E_local) ? (c + bm - 1) / bm : 0;
