@@ -302,6 +302,32 @@ def test_layer_call_equals_the_four_calls(torch, cfg, T):
         assert np.array_equal(a, b), f"{name} differs between the layer call and the four calls"
 
 
+@pytest.mark.parametrize("H", [8192, 16384])
+def test_router_wide_rows(torch, H):
+    """Wide router rows give the small-batch logits kernel 8 and 16 aligned ranges of 32 blocks
+    (the top-k launch adds up to 32 ranges, the selection inside the gate/up launch up to 8): the
+    router call's ids equal the oracle's and its weights are within tolerance; at H=8192 the
+    one-token layer call, which selects inside the gate/up launch, matches the oracle too."""
+    import quantized_moe_routed_amd as moe
+    from quantized_moe_routed_amd.layer import DeviceMatrix
+    _say(f"router with wide rows: H={H}")
+    T, E, k = 3, 64, 4
+    wl = synth.make(synth.custom(T, H, E, 128, k, name=f"wide{H}"), experts=False)
+    ref_ids, ref_w, _ = oracle.route(wl.x, wl.cfg.router_fmt, wl.router[0], wl.bias, wl.k)
+    R = DeviceMatrix(wl.cfg.router_fmt, wl.router[0], 1, E, H, "cuda")
+    rws, _, _ = moe.workspace_size(T, H, 128, k, E, E, moe.ACT_F32)
+    ws = torch.empty(max(rws, 16), dtype=torch.uint8, device="cuda")
+    ids = torch.full((T, k), -1, dtype=torch.int32, device="cuda")
+    w = torch.zeros((T, k), dtype=torch.float32, device="cuda")
+    moe.route(torch.from_numpy(wl.x).cuda(), moe.ACT_F32, T, H, R.qmat(), None, k, ids, w, ws, ws.numel())
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ref_ids), f"ids, H={H}"
+    assert_close(w.cpu().numpy(), ref_w, what=f"router weights H={H}")
+    if H <= 8192:
+        wl1 = synth.make(synth.custom(1, H, 16, 256, k, bias="zipf1.1", name=f"wide{H}_t1"))
+        check_against_oracle(wl1, run(make_layer(wl1), wl1, torch), oracle_expect(wl1), what=f"one token H={H}")
+
+
 @pytest.mark.parametrize("E,k", [(8, 8), (40, 2), (100, 8), (256, 1), (256, 8), (256, 9), (300, 8), (1024, 8)])
 def test_topk_ties_against_a_stable_sort(torch, E, k):
     """Top-k where most choices cross a tie: router bytes of zero (scale 0) make every logit equal
