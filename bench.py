@@ -78,7 +78,6 @@ def input_pool(wl, n_batches, torch):
     return [xs[i * T:(i + 1) * T] for i in range(n_batches)], toks
 
 
-LARGE_MIN = 9    # experts with this many slots or more run on the large-tile kernel (batches of 9+ tokens)
 TRACE_EVERY = 8  # the kernel events of the timed region sample one launch in this many
 
 
@@ -109,7 +108,7 @@ def time_layer(layer, xs, steps, warmup, kernel, torch):
     # per-step loads, outside the timed region: replay the routing of each batch and count the
     # owned experts and slots on each kind of tile
     T = xs[0].shape[0]
-    large_min = LARGE_MIN if T >= LARGE_MIN else 1 << 30
+    large_min = moe.large_tile_min(T) or 1 << 30   # experts of this many slots or more run on large tiles
     owned = None if layer.g2l is None else (layer.g2l >= 0).cpu().numpy()
     d_small, s_small, d_large, s_large = [], [], [], []
     for i in range(min(steps, len(xs))):

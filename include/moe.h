@@ -44,7 +44,7 @@
  *    fallback paths: every expert runs on the fp16 matrix cores, on tiles of up
  *    to 8 slots (4 where the activation rows of 8 slots would not fit the LDS
  *    of two workgroups per compute unit), or of up to 128 slots for experts with
- *    9 or more slots in a batch of 9 or more tokens.
+ *    at least moe_large_tile_min(T) slots.
  *  - Calls that overlap on one stream are ordered; calls sharing a workspace
  *    on different streams race.
  */
@@ -126,6 +126,13 @@ const char* moe_version(void);
  * NULL.  xt selects the expert kernels (their workspace differs).  */
 moe_status moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t k, int32_t E, int32_t E_local,
                               int32_t xt, size_t* route_ws, size_t* group_ws, size_t* forward_ws);
+
+/* Fewest slots of one expert that moe_expert_forward and moe_layer_forward put
+ * on tiles of up to 128 slots in a batch of T tokens; experts with fewer slots
+ * take tiles of up to 8.  0 = small tiles only (T <= 32); 33 for 33 <= T < 256
+ * (experts of more than 4 small tiles); 12 from 256 tokens.  Host only, no GPU
+ * work; the choice changes speed only, never results. */
+int32_t moe_large_tile_min(int32_t T);
 
 /* Router scoring and top-k selection (one token per row of x).
  *   x      : [T, H] fp32 or bf16 (xt), row-major.

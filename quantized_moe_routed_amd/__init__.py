@@ -50,6 +50,8 @@ def _load():
     i32, sz, vp, psz = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
     L.moe_last_error.restype = ctypes.c_char_p
     L.moe_version.restype = ctypes.c_char_p
+    L.moe_large_tile_min.argtypes = [i32]
+    L.moe_large_tile_min.restype = ctypes.c_int32
     L.moe_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, psz, psz, psz]
     L.moe_route.argtypes = [vp, i32, i32, i32, ctypes.POINTER(QMat), vp, i32, vp, vp, vp, sz, vp]
     L.moe_group_tokens.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
@@ -74,7 +76,7 @@ def _load():
 
 lib = _load()
 
-EXPORTS = ("moe_last_error", "moe_version", "moe_workspace_size", "moe_route", "moe_group_tokens",
+EXPORTS = ("moe_last_error", "moe_version", "moe_large_tile_min", "moe_workspace_size", "moe_route", "moe_group_tokens",
            "moe_expert_forward", "moe_combine", "moe_layer_forward", "moe_planar_bytes", "moe_pack_planar", "moe_place_lpt",
            "moe_share_tables", "moe_plan_check", "moe_trace_kernel", "moe_trace_kernel_every")
 
@@ -112,6 +114,11 @@ def _stream(stream):
 
 def qmat(fmt: int, rows: int, cols: int, codes, scales) -> QMat:
     return QMat(fmt, rows, cols, _ptr(codes), _ptr(scales))
+
+
+def large_tile_min(T: int) -> int:
+    """Fewest slots of one expert that go to 128-slot tiles in a batch of T tokens (0: none)."""
+    return int(lib.moe_large_tile_min(T))
 
 
 # ---------------------------------------------------------------- device calls

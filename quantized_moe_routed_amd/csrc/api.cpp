@@ -107,8 +107,13 @@ size_t route_ws_bytes(int T, int E, int H, int fmt = MOE_W_Q8_0) { return align_
 // sums, and the intermediate h (hi, lo) with its block sums.  Block-sum rows
 // are padded to a multiple of 32 blocks.
 constexpr int kLargeTile = 128;   // slots per large tile
-constexpr int kLargeMin = 9;      // experts with at least this many slots use large tiles (batches of 9+ tokens);
-                                  // fewer slots fit one small tile of 8
+
+// Fewest slots of an expert that go to large tiles in a batch of T tokens, 0 = small tiles only.
+// Up to 32 tokens an expert fills at most 4 small tiles of 8 and the large-tile launches would run
+// all but empty; up to 255 tokens the few large tiles form a short, latency-bound launch, so
+// only experts of more than 4 small tiles take one; from 256 tokens the large-tile launches are
+// full, and an expert of 12 or more slots costs less there than on 2 or more small tiles.
+int large_tile_min(int64_t T) { return T <= 32 ? 0 : T < 256 ? 33 : 12; }
 
 int64_t max_tiles(int64_t slots, int64_t experts, int bm) { return (slots + bm - 1) / bm + experts; }
 
@@ -120,11 +125,12 @@ struct TilePlan {
 TilePlan tile_plan(int T, int H, int I, int k, int E_local, int xt) {
   const int64_t slots = (int64_t)T * k;
   TilePlan p{};
-  const bool large = T >= kLargeMin;
-  p.large_min = large ? kLargeMin : 0x7FFFFFFF;
+  const int lmin = large_tile_min(T);
+  const bool large = lmin > 0;
+  p.large_min = large ? lmin : 0x7FFFFFFF;
   p.bm_small = moe::small_tile_rows(H, I, xt == MOE_ACT_F32);
   p.max_small = (int)max_tiles(slots, std::min<int64_t>(E_local, slots), p.bm_small);
-  p.max_large = large ? (int)max_tiles(slots, std::min<int64_t>(E_local, slots / kLargeMin), kLargeTile) : 0;
+  p.max_large = large ? (int)max_tiles(slots, std::min<int64_t>(E_local, slots / lmin), kLargeTile) : 0;
   return p;
 }
 
@@ -229,6 +235,8 @@ moe_status moe_trace_kernel(const char* name, hipEvent_t* start, hipEvent_t* sto
 const char* moe_last_error(void) { return g_err.c_str(); }
 
 const char* moe_version(void) { return "moe-gfx950 0.1"; }
+
+int32_t moe_large_tile_min(int32_t T) { return large_tile_min(T); }
 
 moe_status moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t k, int32_t E, int32_t E_local, int32_t xt,
                               size_t* route_ws, size_t* group_ws, size_t* forward_ws) {

@@ -31,6 +31,14 @@ def test_version():
     assert moe.version().startswith("moe-gfx950")
 
 
+def test_large_tile_threshold_by_batch_size():
+    """Small tiles only up to 32 tokens; up to 255 tokens only experts of more than 4 small tiles
+    take large ones; from 256 tokens experts of 12 or more slots do."""
+    assert [moe.large_tile_min(T) for T in (0, 1, 8, 9, 32)] == [0] * 5
+    assert [moe.large_tile_min(T) for T in (33, 128, 255)] == [33] * 3
+    assert [moe.large_tile_min(T) for T in (256, 2048, 1 << 20)] == [12] * 3
+
+
 def decode_planar(fmt, codes, scales, n, rows, cols):
     """Values of n planar matrices, decoded from the row-group layout as include/moe.h documents it."""
     nb = cols // 32

@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 import synth
+import quantized_moe_routed_amd as moe
 from helpers import assert_close, oracle_expect, sha
 from gpu_util import make_layer, run, torch_mod, x_tensor
 
@@ -76,7 +77,6 @@ def test_cfg3_ragged_tokens(torch):
 
 def test_cfg5_shares_sum_to_full(torch):
     _say("cfg5 shares T=128")
-    import quantized_moe_routed_amd as moe
     wl = synth.make(5)
     owner = moe.place_lpt(wl.load_hist, 2)
     assert np.array_equal(owner, oracle.place_lpt(wl.load_hist, 2))
@@ -152,7 +152,6 @@ def test_t0_is_a_no_op(torch):
 
 def test_host_pointer_is_rejected(torch):
     _say("device check")
-    import quantized_moe_routed_amd as moe
     wl = synth.make(1)
     layer = make_layer(wl)
     b = layer.buffers(wl.T, 0)
@@ -228,7 +227,6 @@ def test_router_token_tiles_ragged(torch, act):
 
 def test_bf16_small_shapes_and_share(torch):
     _say("bf16 small shapes: H=128, I=192, E=8, k=3, T=23; then an owned share and its complement")
-    import quantized_moe_routed_amd as moe
     cfg = synth.custom(23, 128, 8, 192, 3, gate_fmt=2, up_fmt=2, down_fmt=1, router_fmt=1, act="bf16",
                        bias="normal0.5", name="bf16_small")
     wl = synth.make(cfg)
@@ -245,7 +243,7 @@ def test_bf16_small_shapes_and_share(torch):
     assert_close(parts[0] + parts[1], got["out"], "bf16 share A + share B vs full")
 
 
-# ---- large tiles: experts with 9 or more slots ---------------------------------------------
+# ---- large tiles: experts with at least moe_large_tile_min(T) slots -------------------------
 
 _LARGE_CASES = {
     # fp32 activations (hi + lo planes), 2-bit everywhere, a partly filled last code unit (H = 320)
@@ -259,9 +257,13 @@ _LARGE_CASES = {
     # an odd number of blocks per row (H = 2080: 65 blocks), I = 96 (a partial column tile and a
     # partly filled 2-bit unit in the down projection)
     "f32_odd_blocks": (40, 2080, 6, 96, 2, dict(gate_fmt=1, up_fmt=1, down_fmt=2, router_fmt=1, act="f32")),
-    # a batch of 12 tokens (the smallest batches with large tiles): experts of 9-12 slots on large
-    # tiles beside experts on small ones
-    "f32_t12": (12, 256, 4, 128, 3, dict(gate_fmt=2, up_fmt=2, down_fmt=2, router_fmt=1, act="f32")),
+    # a batch of 33 tokens (the smallest batches with large tiles): an expert of all 33 tokens on a
+    # large tile beside one of 32 slots on 4 small tiles
+    "f32_t33": (33, 256, 4, 128, 3, dict(gate_fmt=2, up_fmt=2, down_fmt=2, router_fmt=1, act="f32")),
+    # 256 tokens without router bias (the smallest batches with large tiles from 12 slots):
+    # experts of 12-14 slots on large tiles, of 9-11 on two small tiles, the rest on one
+    "f32_t256_even": (256, 256, 64, 128, 2, dict(gate_fmt=2, up_fmt=2, down_fmt=2, router_fmt=1, act="f32",
+                                                 bias=None)),
 }
 
 
@@ -269,10 +271,12 @@ _LARGE_CASES = {
 def test_large_tiles_against_oracle(torch, name):
     T, H, E, I, k, kw = _LARGE_CASES[name]
     _say(f"large tiles {name}: T={T} H={H} E={E} I={I} k={k}")
-    wl = synth.make(synth.custom(T, H, E, I, k, bias="zipf1.1", name=name, **kw))
+    kw = dict(kw)
+    wl = synth.make(synth.custom(T, H, E, I, k, bias=kw.pop("bias", "zipf1.1"), name=name, **kw))
     got = run(make_layer(wl), wl, torch)
     counts = got["counts"]
-    assert counts.max() >= 9 and ((counts > 0) & (counts < 9)).any()   # both tile kinds in use
+    lmin = moe.large_tile_min(T)
+    assert lmin > 0 and counts.max() >= lmin and ((counts > 0) & (counts < lmin)).any()   # both tile kinds
     if name == "f32_multi_tile":
         assert counts.max() > 2 * 128
     check_against_oracle(wl, got, oracle_expect(wl), what=f"large {name}")
@@ -308,7 +312,6 @@ def test_router_wide_rows(torch, H):
     (the top-k launch adds up to 32 ranges, the selection inside the gate/up launch up to 8): the
     router call's ids equal the oracle's and its weights are within tolerance; at H=8192 the
     one-token layer call, which selects inside the gate/up launch, matches the oracle too."""
-    import quantized_moe_routed_amd as moe
     from quantized_moe_routed_amd.layer import DeviceMatrix
     _say(f"router with wide rows: H={H}")
     T, E, k = 3, 64, 4
@@ -354,7 +357,6 @@ def test_combine_alone(torch, k):
     expert range), H=1000 leaving a partial workgroup.  Dyadic inputs (y in steps of 2^-10 below 1,
     w in steps of 2^-8) make every product and partial sum exact in fp32, so the sum over the owned
     slots is known exactly; random inputs are checked against a float64 sum."""
-    import quantized_moe_routed_amd as moe
     _say(f"combine alone: k={k}")
     rng = np.random.default_rng(100 + k)
     T, H, E = 3, 1000, 40
@@ -404,7 +406,6 @@ def test_layer_call_owned_share(torch, T):
     launches."""
     _say(f"layer call vs four calls: cfg5 share, T={T}")
     wl = synth.make(5, T=T)
-    import quantized_moe_routed_amd as moe
     owner = moe.place_lpt(np.arange(wl.E, dtype=np.int64) % 7 + 1, 2)
     g2l, l2g = moe.share_tables(owner, 0)
     calls, fused = _run_both(make_layer(wl, l2g=l2g, g2l=g2l), wl, torch)
