@@ -8,8 +8,9 @@
 //     acc += (2^-6 d_b) * P_b,
 // and the m-term of 2-bit blocks is one more product over the block index.
 // Here the matrix instruction is v_mfma_f32_32x32x16_f16 (two per block and
-// activation plane), and a workgroup of 4 waves owns 128 slots by 4 x 32 NT2
-// output columns:
+// activation plane), and a workgroup of 8 waves owns 128 slots by 4 x 32 NT2
+// output columns: 4 column groups by 2 row groups of 64 slots (a tile of at
+// most 64 slots gives both row groups its rows, each half the contraction):
 //   * The activation rows of the tile are shared by the 4 waves through LDS.
 //     They are fetched by direct global->LDS loads, in stages of 8 blocks
 //     (4 when the operand has a lo plane), double-buffered: the loads of stage
@@ -74,8 +75,14 @@ struct LargeCfg {
 // so those blocks add exact zeros.
 // Columns past N (N not a multiple of the workgroup's width) are computed on
 // a repeated column and not stored.
+// ks (tiles of at most 64 rows, 8 waves in two row groups of 4): the two row
+// groups take the same rows and split the contraction instead, so that no wave
+// sits idle: row group g runs the stages from g * n_it on, its activation rows
+// sit in LDS row slots 64 g .. 64 g + 63, and at the end row group 1 hands its
+// sums to row group 0 through LDS, which adds them (a fixed order) and stores.
+// A run-time switch, so that it adds no code path of its own.
 template <int F, int NM, bool LO, int MODE, int NT2, int WM, int CG, int MI>
-__device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0, int rows, int ct, int r0,
+__device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0, int rows, int ct, int r0, bool ks,
                                            const int32_t* s_slot, const float* s_inv) {
   using C = LargeCfg<F, NM, LO, MODE, NT2, WM, CG>;
   constexpr int UB = C::UB, P = C::P, SB = C::SB;
@@ -85,6 +92,11 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
   const int c32 = lane & 31, g2 = lane >> 5;
   const int K = a.K, N = a.N, nb = K / 32;
   const int n_units = (nb + UB - 1) / UB;
+  const int n_st = (nb + SB - 1) / SB;   // LDS stages over the contraction
+  // stages this wave's row group runs, from s_base; with ks a half starts on a code unit
+  const int kg = ks ? wave / CG : 0;
+  const int n_it = ks ? (UB > SB ? (n_st + 3) / 4 * 2 : (n_st + 1) / 2) : n_st;
+  const int s_base = kg * n_it;
   const int n0 = ct * C::BN + (wave % CG) * C::WC;
   const int64_t rbytes = Codes<F>::row_bytes(K);
   const int64_t sbytes = Codes<F>::scale_row_bytes(K);
@@ -152,7 +164,7 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
         }
     load_group(g_next);
   };
-  if constexpr (MI > 0) load_group(0);
+  if constexpr (MI > 0) load_group(UB > SB ? s_base * SB / UB : s_base);
 
   // activation rows this lane fetches: rows 16 (GPW wave + j) + lane / 4 of the tile, 16-byte
   // group (lane & 3) ^ swizzle of its LDS slot
@@ -162,7 +174,7 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
   const uint8_t* arow[GPW];
 #pragma unroll
   for (int j = 0; j < GPW; ++j) {
-    int r = 16 * (GPW * wave + j) + rl;
+    int r = 16 * (ks ? wave & 3 : GPW * wave + j) + rl;   // with ks slot group w holds rows 16 (w & 3) ..
     r = r < rows ? r : 0;
     const int64_t src = MODE == MODE_GATEUP ? a.slot_list[p0 + r] / a.k : p0 + r;
     arow[j] = reinterpret_cast<const uint8_t*>(a.a_hi) + (src * K + 8 * grp) * 2;
@@ -170,17 +182,17 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
   const int64_t lo_delta =
       LO ? (reinterpret_cast<const uint8_t*>(a.a_lo) - reinterpret_cast<const uint8_t*>(a.a_hi)) : 0;
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-  auto issue_stage = [&](int st) {
-    const uint32_t sbase = lds0 + (st & 1) * C::STAGE;
+  auto issue_stage = [&](int it) {
+    const uint32_t sbase = lds0 + (it & 1) * C::STAGE;
 #pragma unroll
     for (int pl = 0; pl < P; ++pl)
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
-        const int b = min(st * SB + sb, nb - 1);
+        const int b = min((s_base + it) * SB + sb, nb - 1);
 #pragma unroll
         for (int j = 0; j < GPW; ++j) {
-          const int rg = 16 * (GPW * wave + j);
-          if (rg < rows) {
+          const int rg = 16 * (GPW * wave + j);   // LDS row slot
+          if (rg - 64 * kg < rows) {
             const uint32_t dst = sbase + (uint32_t)(((pl * SB + sb) * kLgRows + rg) * 64);
             dma16(arow[j] + pl * lo_delta + 64 * (int64_t)b, __builtin_amdgcn_readfirstlane(dst));
           }
@@ -203,8 +215,6 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
       for (int mt = 0; mt < NM; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[mi][nt][mt][e] = 0.0f;
-  const int nbs = (nb + SB - 1) / SB * SB;   // blocks the loop runs over
-  const int n_st = nbs / SB;
 
   // The products of one block are taken pair by pair (row fragment, output matrix/tile); the
   // matrix instructions of pair q are issued between the fp32 scale-and-add of pair q - 1, so the
@@ -235,8 +245,8 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
   // block's codes, and only then issue the next stage's activation loads.  The compiler's own
   // waits for weight loads then all fall before the direct LDS loads, which it does not see;
   // a wait placed after them would also wait for them.
-  for (int b0 = 0; b0 < nbs; b0 += SB) {
-    const int st = b0 / SB;
+  for (int it = 0; it < n_it; ++it) {
+    const int st = s_base + it, b0 = st * SB;
     wait_vmem();
     __syncthreads();   // stage st is in LDS; every wave is done with the buffer refilled next
     uint4 bf0[NT2][NM][2];
@@ -244,7 +254,7 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
     if constexpr (MI > 0) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        rb[h] = lds0 + (st & 1) * C::STAGE + r0 * 64 + aoff[h];
+        rb[h] = lds0 + (it & 1) * C::STAGE + (ks ? 64 * kg : r0) * 64 + aoff[h];
         asm volatile("" : "+v"(rb[h]));
       }
       read_frags(afn, 0, 0);
@@ -280,7 +290,7 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (st + 1 < n_st) issue_stage(st + 1);
+    if (it + 1 < n_it) issue_stage(it + 1);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (MI > 0) {
 #pragma unroll
@@ -331,7 +341,7 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
   }
   if constexpr (MI > 0) fold(MI * QP - 1, pprev, dprev);
 
-  if constexpr (Codes<F>::kHasM && MI > 0) {
+  if constexpr (Codes<F>::kHasM && MI > 0) if (kg == 0) {
     // sum_b m_b (sigma S_b): block index as the contraction, 32 blocks per step
     const int mlen = n_units * UB;   // blocks covered by the units (the rest of a step is zero)
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
@@ -373,6 +383,34 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
           }
       }
     }
+  }
+
+  if (ks) {
+    // row group 1's sums to row group 0, element by element through LDS (the stages are free once
+    // every wave has passed the first barrier)
+    float* red = reinterpret_cast<float*>(lds);
+    const int cg = wave % CG;
+    __syncthreads();
+    if (kg == 1) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nt = 0; nt < NT2; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) red[((((cg * MI + mi) * NT2 + nt) * NM + mt) * 16 + e) * 64 + lane] = acc[mi][nt][mt][e];
+    }
+    __syncthreads();
+    if (kg == 1) return;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int nt = 0; nt < NT2; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[mi][nt][mt][e] += red[((((cg * MI + mi) * NT2 + nt) * NM + mt) * 16 + e) * 64 + lane];
   }
 
   // epilogue: acc[mi][nt][mt][e] is row r0 + 32 mi + 8 (e / 4) + 4 g2 + e % 4, column n0 + 32 nt + c32
@@ -448,9 +486,10 @@ __global__ __launch_bounds__((LargeCfg<F, NM, LO, MODE, NT2, WM, CG>::THREADS), 
     s_inv[threadIdx.x] = MODE == MODE_GATEUP ? 1.0f / a.sigma[sl / a.k] : 1.0f;   // a power of two: exact
   }
   const int wm = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) / CG;
-  const int r0 = wm * 32 * C::MIMAX;
+  int r0 = wm * 32 * C::MIMAX;
   const int mi = min(max((tl.z - r0 + 31) / 32, 0), C::MIMAX);
-#define MOE_TILE(M) large_tile<F, NM, LO, MODE, NT2, WM, CG, M>(a, tl.x, tl.y, tl.z, ct, r0, s_slot, s_inv)
+  bool ks = false;
+#define MOE_TILE(M) large_tile<F, NM, LO, MODE, NT2, WM, CG, M>(a, tl.x, tl.y, tl.z, ct, r0, ks, s_slot, s_inv)
   if constexpr (C::MIMAX == 4) {
     switch (mi) {
       case 1: MOE_TILE(1); break;
@@ -459,11 +498,13 @@ __global__ __launch_bounds__((LargeCfg<F, NM, LO, MODE, NT2, WM, CG>::THREADS), 
       default: MOE_TILE(4); break;
     }
   } else {
-    switch (mi) {
-      case 0: MOE_TILE(0); break;
-      case 1: MOE_TILE(1); break;
-      default: MOE_TILE(2); break;
-    }
+    static_assert(C::MIMAX != 2 || (CG == 4 && C::GPW == 1), "the split contraction: 8 waves, one slot group each");
+    static_assert(CG * C::MIMAX * NT2 * NM * 16 * 64 * 4 <= 2 * C::STAGE, "row group 1's sums fit the stages");
+    // at most 64 rows: both row groups on them, each on half the contraction
+    ks = tl.z <= 64;
+    if (ks) r0 = 0;
+    if ((ks ? tl.z : mi * 32) <= 32) MOE_TILE(1);
+    else MOE_TILE(2);
   }
 #undef MOE_TILE
 }
