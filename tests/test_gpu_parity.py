@@ -10,6 +10,7 @@ import pytest
 import oracle
 import synth
 import quantized_moe_routed_amd as moe
+import helpers
 from helpers import assert_close, oracle_expect, sha
 from gpu_util import make_layer, run, torch_mod, x_tensor
 
@@ -280,6 +281,39 @@ def test_large_tiles_against_oracle(torch, name):
     if name == "f32_multi_tile":
         assert counts.max() > 2 * 128
     check_against_oracle(wl, got, oracle_expect(wl), what=f"large {name}")
+
+
+# slots per expert around the large kernel's row-group and tile edges (a batch of 429 tokens, one
+# slot each, so experts of 12 or more slots take large tiles): 32 and 33 (one and two 32-row
+# fragments, contraction split between the row groups), 64 (the split's largest tile), 65 and 96
+# (second row group on one fragment), 129 (a full tile and a split tile of one row), 10 (two small
+# tiles), 0
+_EDGE_COUNTS = [32, 33, 64, 65, 96, 129, 10, 0]
+
+
+@pytest.mark.parametrize("act,fm", [("f32", (2, 2, 1)), ("bf16", (1, 1, 2))])
+def test_large_tile_row_edges(torch, act, fm):
+    """Expert loads set by hand at the large kernel's row-group edges: every y_slot row equals the
+    oracle's expert output for its slot, within tolerance."""
+    T, E = sum(_EDGE_COUNTS), len(_EDGE_COUNTS)
+    _say(f"large-tile row edges {act} fmts={fm}: T={T} counts={_EDGE_COUNTS}")
+    assert moe.large_tile_min(T) == 12
+    wl = synth.make(synth.custom(T, 256, E, 128, 1, gate_fmt=fm[0], up_fmt=fm[1], down_fmt=fm[2], router_fmt=1,
+                                 act=act, name=f"edges_{act}"))
+    ids = np.repeat(np.arange(E, dtype=np.int32), _EDGE_COUNTS)
+    ids = ids[np.random.default_rng(7).permutation(T)].reshape(T, 1)
+    layer = make_layer(wl)
+    from quantized_moe_routed_amd.layer import act_code
+    x = x_tensor(wl, torch)
+    b = layer.buffers(T, act_code(x))
+    b.ids.copy_(torch.from_numpy(ids))
+    layer.group(b)
+    layer.forward(x, b)
+    torch.cuda.synchronize()
+    assert np.array_equal(b.counts.cpu().numpy(), np.array(_EDGE_COUNTS))
+    rows = oracle.forward_slots(helpers.fmts(wl), wl.gate, wl.up, wl.down, wl.x, ids, range(T))
+    ref = np.stack([rows[s] for s in range(T)])
+    assert_close(b.y_slot.cpu().numpy()[:T], ref, f"edges {act} y_slot")
 
 
 def _run_both(layer, wl, torch):
