@@ -212,9 +212,12 @@ moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, in
  * While set (on the calling thread), the i-th launch of the kernel called
  * `name` gets hipEventRecord(start[i]) before and hipEventRecord(stop[i])
  * after it on the call's stream, for i < n; *count holds how many launches
- * were recorded.  Kernel names: route_logits, route_topk, group, prep, front
- * (selection to operands in one launch, small batches), ffn_gateup, ffn_down
- * (small tiles), ffn_gateup_large, ffn_down_large, combine.  The caller owns
+ * were recorded.  The expert kernels (ffn_*) instead hand start[i] and stop[i]
+ * to the launch itself (hipExtLaunchKernel), so that they hold the kernel's
+ * own start and end, the interval a profiler reports.  Kernel names:
+ * route_logits, route_topk, group, prep, front (selection to operands in one
+ * launch, small batches), ffn_gateup, ffn_down (small tiles),
+ * ffn_gateup_large, ffn_down_large, combine.  The caller owns
  * the events and must keep them, and count, alive while tracing; n <= 0
  * switches tracing off. */
 moe_status moe_trace_kernel(const char* name, hipEvent_t* start, hipEvent_t* stop, int32_t n, int32_t* count);

@@ -92,6 +92,7 @@ struct Trace {
   int every = 1;       // record launches 0, every, 2 every, ...
   int seen = 0;        // launches of the kernel since tracing was set
   bool armed = false;  // the current launch is being recorded
+  bool stamped = false;  // ... by the launch itself (launch_stamped)
   int32_t* count = nullptr;
 };
 thread_local Trace g_trace;
@@ -187,18 +188,26 @@ moe_status check_qmat(const moe_qmat& m, const char* name, int rows, int cols, b
 }  // namespace
 
 namespace moe {
-void trace_pre(const char* name, hipStream_t s) {
+thread_local StampEvents g_stamp;
+StampEvents& stamp_events() { return g_stamp; }
+
+void trace_pre(const char* name, hipStream_t s, bool stamped) {
   Trace& t = g_trace;
   if (t.n > 0 && t.name == name) {
     t.armed = t.seen % t.every == 0 && *t.count < t.n;
-    if (t.armed) (void)hipEventRecord(t.start[*t.count], s);
+    t.stamped = stamped;
+    if (t.armed) {
+      if (stamped) g_stamp = StampEvents{t.start[*t.count], t.stop[*t.count]};
+      else (void)hipEventRecord(t.start[*t.count], s);
+    }
   }
 }
 void trace_post(const char* name, hipStream_t s) {
   Trace& t = g_trace;
   if (t.n > 0 && t.name == name) {
     if (t.armed) {
-      (void)hipEventRecord(t.stop[*t.count], s);
+      if (!t.stamped) (void)hipEventRecord(t.stop[*t.count], s);
+      g_stamp = StampEvents{};
       ++*t.count;
       t.armed = false;
     }

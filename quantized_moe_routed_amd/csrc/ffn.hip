@@ -433,8 +433,7 @@ static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  kern<<<dim3(t.N / (16 * kNT), max_tiles + (SEL ? 1 : 0)), kFfnThreads, lds, s>>>(t);
-  return hipGetLastError();
+  return launch_stamped(kern, dim3(t.N / (16 * kNT), max_tiles + (SEL ? 1 : 0)), dim3(kFfnThreads), lds, s, t);
 }
 
 int small_tile_rows(int H, int I, bool f32_act) {
@@ -464,7 +463,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   (one ? launch_small_t<F, 2, LO, MODE_GATEUP, true, true>(t, a.max_small, s)                       \
        : launch_small_t<F, 2, LO, MODE_GATEUP, false, true>(t, a.max_small, s))
   t.tiles = a.small; t.tile_tok = a.small_tok; t.n_tiles = a.n_small;
-  trace_pre("ffn_gateup", s);
+  trace_pre("ffn_gateup", s, true);
   if (a.sel) {
     t.sel = *a.sel;
     if (a.fg == FMT_Q2SM) err = lo ? MOE_SMALL_SEL(FMT_Q2SM, true) : MOE_SMALL_SEL(FMT_Q2SM, false);
@@ -478,7 +477,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (err != hipSuccess) return err;
   if (a.max_large > 0) {
     t.tiles = a.large; t.n_tiles = a.n_large;
-    trace_pre("ffn_gateup_large", s);
+    trace_pre("ffn_gateup_large", s, true);
     err = launch_large(t, a.fg, MODE_GATEUP, lo, a.max_large, s);
     trace_post("ffn_gateup_large", s);
     if (err != hipSuccess) return err;
@@ -488,13 +487,13 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   t.K = a.I; t.N = a.H; t.nb32 = a.nb32I; t.w0 = a.down; t.w1 = a.down;
   t.y = a.y;
   t.tiles = a.small; t.n_tiles = a.n_small;
-  trace_pre("ffn_down", s);
+  trace_pre("ffn_down", s, true);
   err = a.fd == FMT_Q2SM ? MOE_SMALL(FMT_Q2SM, 1, true, MODE_DOWN) : MOE_SMALL(FMT_Q8_0, 1, true, MODE_DOWN);
   trace_post("ffn_down", s);
   if (err != hipSuccess) return err;
   if (a.max_large > 0) {
     t.tiles = a.large; t.n_tiles = a.n_large;
-    trace_pre("ffn_down_large", s);
+    trace_pre("ffn_down_large", s, true);
     err = launch_large(t, a.fd, MODE_DOWN, true, a.max_large, s);
     trace_post("ffn_down_large", s);
   }

@@ -522,8 +522,7 @@ static hipError_t launch_large_t(const FfnTileArgs& t, int max_tiles, hipStream_
   }
   const int n_ct = (t.N + C::BN - 1) / C::BN;
   const int grid = 8 * n_ct * ((max_tiles + 7) / 8);
-  ffn_large_kernel<F, NM, LO, MODE, NT2, WM, CG><<<grid, C::THREADS, lds, s>>>(t, n_ct);
-  return hipGetLastError();
+  return launch_stamped(ffn_large_kernel<F, NM, LO, MODE, NT2, WM, CG>, dim3(grid), dim3(C::THREADS), lds, s, t, n_ct);
 }
 
 // Two row groups of waves (8 waves, two per SIMD): each wave holds half the accumulators, and

@@ -1,5 +1,6 @@
 // Host-side launchers of the gfx950 kernels (internal to libmoe).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -10,9 +11,26 @@ struct QMat;
 struct SelArgs;   // smallsel.h
 
 // Optional event tracing of one kernel (see moe_trace_kernel): record an event
-// on the stream before and after the launch of kernel `name`.
-void trace_pre(const char* name, hipStream_t s);
+// on the stream before and after the launch of kernel `name`.  With stamped,
+// the launch in between goes through launch_stamped, which hands the events
+// to the runtime instead: they then carry the kernel's own start and end, the
+// interval a profiler reports, without the stream's dispatch gaps around it.
+void trace_pre(const char* name, hipStream_t s, bool stamped = false);
 void trace_post(const char* name, hipStream_t s);
+
+// Events for the next launch_stamped (both null unless trace_pre armed them).
+struct StampEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+StampEvents& stamp_events();
+
+template <typename... KArgs, typename... Args>
+hipError_t launch_stamped(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t s, Args... args) {
+  StampEvents& ev = stamp_events();
+  hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0u, args...);
+  ev = StampEvents{};
+  return hipGetLastError();
+}
 
 hipError_t launch_route(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
                         int k, int32_t* ids, float* w, void* ws, hipStream_t s);
