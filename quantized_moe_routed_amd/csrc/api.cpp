@@ -206,9 +206,12 @@ void trace_post(const char* name, hipStream_t s) {
   Trace& t = g_trace;
   if (t.n > 0 && t.name == name) {
     if (t.armed) {
+      // a stamped launch consumes its events; ones still here belong to a launch that never
+      // happened (an error before it), and are not counted
+      const bool recorded = !t.stamped || g_stamp.start == nullptr;
       if (!t.stamped) (void)hipEventRecord(t.stop[*t.count], s);
       g_stamp = StampEvents{};
-      ++*t.count;
+      if (recorded) ++*t.count;
       t.armed = false;
     }
     ++t.seen;

@@ -445,3 +445,28 @@ def test_layer_call_owned_share(torch, T):
     calls, fused = _run_both(make_layer(wl, l2g=l2g, g2l=g2l), wl, torch)
     for name, a, b in zip(("ids", "w", "counts", "offsets", "slot_list", "y_slot", "out"), calls, fused):
         assert np.array_equal(a, b), f"{name} differs between the layer call and the four calls"
+
+
+@pytest.mark.parametrize("name", ["ffn_gateup", "combine"])
+def test_kernel_trace_records_each_launch(torch, name):
+    """moe_trace_kernel_every records launches 0, 2, 4 of a kernel: stamped by the launch itself
+    (expert kernels) or by events on the stream around it (the others); each recorded interval is
+    positive and no longer than the whole layer call that contains it."""
+    _say(f"kernel trace {name}")
+    wl = synth.make(3, T=32)
+    layer = make_layer(wl)
+    from quantized_moe_routed_amd.layer import act_code
+    x = x_tensor(wl, torch)
+    b = layer.buffers(wl.T, act_code(x))
+    layer.run(x, b)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with moe.KernelTrace(name, 4, 2) as tr:
+        t0.record()
+        for _ in range(5):
+            layer.run(x, b)
+        t1.record()
+    times = tr.times_ms()
+    assert tr.count.value == 3 and len(times) == 3
+    total = t0.elapsed_time(t1)
+    assert all(0.0 < t < total for t in times), (times, total)
