@@ -40,7 +40,9 @@ WORKLOADS = {
     "batched_decode": 3,
     "prefill": 4,
     "ep_share": 5,
+    "table_batched": 3,
 }
+TABLE_V = 8192   # rows of the synthetic token-id routing table
 
 
 def log(msg):
@@ -81,15 +83,18 @@ def input_pool(wl, n_batches, torch):
 TRACE_EVERY = 8  # the kernel events of the timed region sample one launch in this many
 
 
-def time_layer(layer, xs, steps, warmup, kernel, torch):
+def time_layer(layer, xs, steps, warmup, kernel, torch, run=None, route=None):
     """Run warmup + steps layer calls cycling through xs; returns the step time
     (ms), the average duration of `kernel` (ms), and per batch the mean number
-    of owned experts and of slots on small tiles and on large tiles."""
+    of owned experts and of slots on small tiles and on large tiles.  run(i, b) and route(i, b)
+    replace the layer call and the routing of batch i (table routing)."""
     import quantized_moe_routed_amd as moe
     from quantized_moe_routed_amd.layer import act_code
     b = layer.buffers(xs[0].shape[0], act_code(xs[0]))
+    run = run or (lambda i, b: layer.run(xs[i], b))
+    route = route or (lambda i, b: layer.route(xs[i], b))
     for i in range(warmup):
-        layer.run(xs[i % len(xs)], b)
+        run(i % len(xs), b)
     torch.cuda.synchronize()
     # events around every TRACE_EVERY-th launch of the kernel only: each pair of events costs the
     # stream a few microseconds, which would otherwise be charged to every step
@@ -100,7 +105,7 @@ def time_layer(layer, xs, steps, warmup, kernel, torch):
     with trace:
         start.record()
         for i in range(steps):
-            layer.run(xs[(warmup + i) % len(xs)], b)
+            run((warmup + i) % len(xs), b)
         end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / steps
@@ -112,7 +117,7 @@ def time_layer(layer, xs, steps, warmup, kernel, torch):
     owned = None if layer.g2l is None else (layer.g2l >= 0).cpu().numpy()
     d_small, s_small, d_large, s_large = [], [], [], []
     for i in range(min(steps, len(xs))):
-        layer.route(xs[(warmup + i) % len(xs)], b)
+        route((warmup + i) % len(xs), b)
         layer.group(b)
         c = b.counts.cpu().numpy()
         if owned is not None:
@@ -157,8 +162,17 @@ def measure(name, steps, warmup, torch):
     gateup_per_expert = (layer.gate.nbytes() + layer.up.nbytes()) // layer.E_local
     bf16 = wl.cfg.act == "bf16"
     kernel = "ffn_gateup_large" if name == "prefill" else "ffn_gateup"
+    run = route = None
+    if name == "table_batched":
+        # table routing: each batch's token ids index a seeded [TABLE_V, k] table of distinct experts
+        import synth
+        table = torch.from_numpy(synth.route_table(0, TABLE_V, wl.E, k)).cuda()
+        tok = torch.from_numpy(synth.token_ids(0, T * len(xs), TABLE_V)).cuda()
+        tids = [tok[i * T:(i + 1) * T] for i in range(len(xs))]
+        run = lambda i, b: layer.run_table(xs[i], b, tids[i], table)
+        route = lambda i, b: layer.route_table(xs[i], b, tids[i], table)
     log(f"{name}: timing {steps} steps")
-    ms, kms, d_small, s_small, d_large, s_large = time_layer(layer, xs, steps, warmup, kernel, torch)
+    ms, kms, d_small, s_small, d_large, s_large = time_layer(layer, xs, steps, warmup, kernel, torch, run, route)
     slots = s_small + s_large
     router_bytes = layer.router.nbytes()
     x_bytes = T * H * (2 if bf16 else 4)
@@ -312,10 +326,10 @@ def main():
     wl, head = measure(args.workload, args.steps, args.warmup, torch)
     others = {}
     if not args.only:
-        for name in ("batched_decode", "prefill", "ep_share", "decode"):
+        for name in ("batched_decode", "prefill", "ep_share", "table_batched", "decode"):
             if name == args.workload:
                 continue
-            steps = {"prefill": 20, "batched_decode": 100, "ep_share": 50, "decode": 200}[name]
+            steps = {"prefill": 20, "batched_decode": 100, "ep_share": 50, "table_batched": 100, "decode": 200}[name]
             _, r = measure(name, steps, 5, torch)
             others[name] = r
     T = head["T"]
@@ -329,6 +343,8 @@ def main():
                    "bias, bf16 activations on matrix cores",
         "ep_share": "expert-parallel share: T=128, 128 of 256 experts owned (LPT), H=4096, I=2048, top-8, "
                     "Q2SM gate/up, Q8_0 down, fp32 activations; partial output",
+        "table_batched": "batched decode with table routing: T=32, experts from a seeded 8192-row token-id table "
+                         "of 8 distinct experts, shapes and formats of batched decode",
     }[args.workload]
     result = {
         "metric": "MoE layer tokens/s at 1 MI355X; decode HBM GB/s and prefill MFMA % of peak",

@@ -149,6 +149,28 @@ moe_status moe_route(const void* x, int32_t xt, int32_t T, int32_t H, const moe_
                      const float* bias, int32_t k, int32_t* ids, float* w, void* ws, size_t ws_bytes,
                      hipStream_t s);
 
+/* Table (hash) routing: the experts of token t are row token_ids[t] of a fixed
+ * [V, k] token-id table, in the row's order, in place of the top k (the
+ * expert-parallel page, "Stage 0": the model's first layers route by a fixed
+ * token-id table).  The pages give no weight rule for such routes; the
+ * reading taken is the learned routes' own: w[t,j] = sigmoid(z) of expert
+ * ids[t,j] renormalised over the row, z the logit of moe_route (bias
+ * included), in fp64 and rounded.  A table row equal to a token's top k gives
+ * moe_route's ids and weights bit for bit.
+ *   token_ids : [T] int32 device; values outside 0..V-1 are clamped.
+ *   table     : [V, k] int32 device; entries must lie in 0..E-1 and be
+ *               distinct within a row (check once on the host with
+ *               moe_table_check); entries outside are clamped, so no read
+ *               leaves the arrays.
+ * Other arguments, workspace and limits as moe_route. */
+moe_status moe_route_table(const void* x, int32_t xt, int32_t T, int32_t H, const moe_qmat* router,
+                           const float* bias, const int32_t* token_ids, const int32_t* table, int32_t V,
+                           int32_t k, int32_t* ids, float* w, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Host check of a routing table [V, k] (host memory): every entry in 0..E-1,
+ * no expert twice in a row.  MOE_ERR_ARG names the first offending entry. */
+moe_status moe_table_check(const int32_t* table, int32_t V, int32_t k, int32_t E);
+
 /* Group the T*k routing slots (slot s = t*k + j) by expert.
  *   counts    : [E] int32 out, slots routed to each expert (the per-expert token
  *               load; the number of non-zero entries is the count of distinct

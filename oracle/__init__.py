@@ -118,6 +118,26 @@ def route(x: np.ndarray, router_fmt: int, router: np.ndarray, bias: Optional[np.
     return ids, w, z
 
 
+def route_table(x: np.ndarray, router_fmt: int, router: np.ndarray, bias: Optional[np.ndarray],
+                token_ids: np.ndarray, table: np.ndarray):
+    """Table routing (aeonmindai/arc PR #89, "Stage 0": the first layers of the model route by a
+    fixed token-id table).  The experts of token t are row token_ids[t] of table [V, k], in the
+    row's order.  The page gives no weight rule; the reading is the learned routes' rule:
+    sigmoid of each expert's logit (the same logits as route(), bias included), renormalised over
+    the row, in fp64, rounded to fp32.  Returns ids [T,k] int32 and w [T,k] fp32."""
+    table = np.asarray(table, dtype=np.int32)
+    k = table.shape[1]
+    _, _, z = route(x, router_fmt, router, bias, 1)
+    ids = table[np.asarray(token_ids, dtype=np.int64)]
+    w = np.empty(ids.shape, dtype=np.float32)
+    for t in range(ids.shape[0]):
+        s = [1.0 / (1.0 + np.exp(-float(z[t, e]))) for e in ids[t]]
+        tot = sum(s)
+        for j in range(k):
+            w[t, j] = np.float32(s[j] / tot)
+    return ids.astype(np.int32), w
+
+
 # ---------------------------------------------------------------- group
 def group(ids: np.ndarray, E: int):
     """Stable grouping of slots s = t*k + j by expert id."""

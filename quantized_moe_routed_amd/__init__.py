@@ -54,6 +54,8 @@ def _load():
     L.moe_large_tile_min.restype = ctypes.c_int32
     L.moe_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, psz, psz, psz]
     L.moe_route.argtypes = [vp, i32, i32, i32, ctypes.POINTER(QMat), vp, i32, vp, vp, vp, sz, vp]
+    L.moe_route_table.argtypes = [vp, i32, i32, i32, ctypes.POINTER(QMat), vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+    L.moe_table_check.argtypes = [vp, i32, i32, i32]
     L.moe_group_tokens.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.moe_expert_forward.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(Experts), vp, i32, i32,
                                      vp, vp, vp, vp, vp, sz, vp]
@@ -68,7 +70,7 @@ def _load():
     L.moe_trace_kernel.argtypes = [ctypes.c_char_p, vp, vp, i32, ctypes.POINTER(ctypes.c_int32)]
     L.moe_trace_kernel_every.argtypes = [ctypes.c_char_p, vp, vp, i32, i32, ctypes.POINTER(ctypes.c_int32)]
     for f in ("moe_trace_kernel", "moe_trace_kernel_every", "moe_workspace_size", "moe_route", "moe_group_tokens", "moe_expert_forward", "moe_combine",
-              "moe_layer_forward",
+              "moe_layer_forward", "moe_route_table", "moe_table_check",
               "moe_planar_bytes", "moe_pack_planar", "moe_place_lpt", "moe_share_tables", "moe_plan_check"):
         getattr(L, f).restype = ctypes.c_int
     return L
@@ -78,7 +80,8 @@ lib = _load()
 
 EXPORTS = ("moe_last_error", "moe_version", "moe_large_tile_min", "moe_workspace_size", "moe_route", "moe_group_tokens",
            "moe_expert_forward", "moe_combine", "moe_layer_forward", "moe_planar_bytes", "moe_pack_planar", "moe_place_lpt",
-           "moe_share_tables", "moe_plan_check", "moe_trace_kernel", "moe_trace_kernel_every")
+           "moe_share_tables", "moe_plan_check", "moe_trace_kernel", "moe_trace_kernel_every", "moe_route_table",
+           "moe_table_check")
 
 
 def last_error() -> str:
@@ -223,6 +226,17 @@ class KernelTrace:
         import torch
         torch.cuda.synchronize()
         return [a.elapsed_time(b) for a, b in zip(self._ev0[: self.count.value], self._ev1[: self.count.value])]
+
+
+def route_table(x, xt, T, H, router: QMat, bias, token_ids, table, V, k, ids, w, ws, ws_bytes, stream=None):
+    _check(lib.moe_route_table(_ptr(x), xt, T, H, ctypes.byref(router), _ptr(bias), _ptr(token_ids), _ptr(table), V,
+                               k, _ptr(ids), _ptr(w), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def table_check(table: np.ndarray, E: int):
+    table = np.ascontiguousarray(table, dtype=np.int32)
+    V, k = table.shape
+    _check(lib.moe_table_check(_ptr(table), V, k, E))
 
 
 def plan_check(g2l: np.ndarray, E_local: int):

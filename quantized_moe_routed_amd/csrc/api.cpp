@@ -475,6 +475,26 @@ moe_status moe_route(const void* x, int32_t xt, int32_t T, int32_t H, const moe_
   return ok();
 }
 
+moe_status moe_route_table(const void* x, int32_t xt, int32_t T, int32_t H, const moe_qmat* router, const float* bias,
+                           const int32_t* token_ids, const int32_t* table, int32_t V, int32_t k, int32_t* ids,
+                           float* w, void* ws, size_t ws_bytes, hipStream_t s) {
+  const char* fn = "moe_route_table";
+  if (V < 1) return fail(MOE_ERR_ARG, "%s: V = %d, the table needs a row", fn, V);
+  if (T > 0 && (!token_ids || !table)) return fail(MOE_ERR_ARG, "%s: token_ids and table must not be NULL", fn);
+  moe_status st = route_check(fn, x, xt, T, H, router, bias, k, ids, w, ws, ws_bytes, s);
+  if (st) return st;
+  if (T == 0) return ok();
+  DevCheck dc;
+  if ((st = stream_device(s, &dc.dev))) return st;
+  dc(token_ids, "token_ids");
+  dc(table, "table");
+  if (dc.st) return dc.st;
+  hipError_t e = moe::launch_route_table(x, xt, T, H, router->fmt, qm(*router), bias, token_ids, table, V, k, ids, w,
+                                         ws, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_route_table launch");
+  return ok();
+}
+
 moe_status moe_group_tokens(const int32_t* ids, int32_t T, int32_t k, int32_t E, int32_t* counts, int32_t* offsets,
                             int32_t* slot_list, void* ws, size_t ws_bytes, hipStream_t s) {
   (void)ws;
@@ -722,6 +742,19 @@ moe_status moe_share_tables(const int32_t* owner, int32_t E, int32_t share, cons
     l2g[l] = owned[l];
   }
   *E_local = (int32_t)owned.size();
+  return ok();
+}
+
+moe_status moe_table_check(const int32_t* table, int32_t V, int32_t k, int32_t E) {
+  if (!table || V < 1 || k < 1 || E < 1 || k > E) return fail(MOE_ERR_ARG, "moe_table_check: bad arguments");
+  std::vector<int> row_of(E, -1);   // the last row that named each expert
+  for (int v = 0; v < V; ++v)
+    for (int j = 0; j < k; ++j) {
+      const int e = table[(int64_t)v * k + j];
+      if (e < 0 || e >= E) return fail(MOE_ERR_ARG, "moe_table_check: table[%d][%d] = %d outside 0..%d", v, j, e, E - 1);
+      if (row_of[e] == v) return fail(MOE_ERR_ARG, "moe_table_check: expert %d twice in row %d", e, v);
+      row_of[e] = v;
+    }
   return ok();
 }
 

@@ -32,6 +32,11 @@ hipError_t launch_stamped(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t 
   return hipGetLastError();
 }
 
+// Table routing: the experts of token t are row token_ids[t] of table [V, k]; logits and weights
+// as launch_route's (ws the same size).
+hipError_t launch_route_table(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
+                              const int32_t* token_ids, const int32_t* table, int V, int k, int32_t* ids, float* w,
+                              void* ws, hipStream_t s);
 hipError_t launch_route(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
                         int k, int32_t* ids, float* w, void* ws, hipStream_t s);
 size_t route_ws_need(int T, int E, int H, int fmt);   // workspace bytes of launch_route

@@ -543,6 +543,53 @@ hipError_t launch_logits(const void* x, int act, int T, int H, int fmt, const QM
   return err;
 }
 
+// Table routing, one wave per token: lane j < k takes expert table[token_ids[t]][j] (both indices
+// clamped into range, so no read leaves the arrays), its logit as the selection forms it (the S
+// partial sums added pairwise, level by level, then the bias; S = 0: z holds the logit), and the
+// weights by the top-k's rule, in the table row's order.
+__global__ __launch_bounds__(256) void route_table_kernel(const float* __restrict__ z, int S,
+                                                          const float* __restrict__ bias, int T, int E, int k,
+                                                          const int32_t* __restrict__ token_ids,
+                                                          const int32_t* __restrict__ table, int V,
+                                                          int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int t = blockIdx.x * 4 + (int)threadIdx.x / kWave;
+  if (t >= T) return;   // the whole wave
+  const int lane = threadIdx.x % kWave;
+  int e = 0;
+  float zl = 0.0f;
+  if (lane < k) {
+    const int tok = min(max(token_ids[t], 0), V - 1);
+    e = min(max(table[(int64_t)tok * k + lane], 0), E - 1);
+    if (S == 0) {
+      zl = z[(int64_t)t * E + e];
+    } else {
+      float v[kMaxRanges];
+#pragma unroll
+      for (int j = 0; j < kMaxRanges; ++j) v[j] = j < S ? z[((int64_t)j * T + t) * E + e] : 0.0f;
+#pragma unroll
+      for (int h = 1; h < kMaxRanges; h <<= 1)
+#pragma unroll
+        for (int j = 0; j + h < kMaxRanges; j += 2 * h) v[j] = j + h < S ? v[j] + v[j + h] : v[j];
+      zl = bias ? v[0] + bias[e] : v[0];
+    }
+  }
+  topk_store(k, t, e, float_key(zl), ids, w);
+}
+
+hipError_t launch_route_table(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
+                              const int32_t* token_ids, const int32_t* table, int V, int k, int32_t* ids, float* w,
+                              void* ws, hipStream_t s) {
+  int S = 0;
+  hipError_t err = launch_logits(x, act, T, H, fmt, router, bias, ws, &S, s, nullptr);
+  if (err != hipSuccess) return err;
+  if (S > kMaxRanges) return hipErrorInvalidValue;
+  trace_pre("route_table", s);
+  route_table_kernel<<<(T + 3) / 4, 256, 0, s>>>(reinterpret_cast<const float*>(ws), S, bias, T, router.rows, k,
+                                                  token_ids, table, V, ids, w);
+  trace_post("route_table", s);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const void* x, int act, int T, int H, int fmt, const QMat& router, const float* bias,
                         int k, int32_t* ids, float* w, void* ws, hipStream_t s) {
   const int E = router.rows;

@@ -16,7 +16,7 @@ import torch
 
 from . import (ACT_BF16, ACT_F32, W_F32, Experts, combine, expert_forward, group_tokens, layer_forward, pack_planar,
                plan_check,
-               qmat, route, workspace_size)
+               qmat, route, route_table, table_check, workspace_size)
 
 
 def _to_dev(a: Optional[np.ndarray], device) -> Optional[torch.Tensor]:
@@ -108,6 +108,11 @@ class MoELayer:
         route(x, b.xt, b.T, self.H, self._router_q, self.bias, self.k, b.ids, b.w, b.route_ws,
               b.route_ws.numel(), stream)
 
+    def route_table(self, x: torch.Tensor, b: Buffers, token_ids: torch.Tensor, table: torch.Tensor, stream=None):
+        """Table routing: token t takes the experts of row token_ids[t] of table [V, k] (device)."""
+        route_table(x, b.xt, b.T, self.H, self._router_q, self.bias, token_ids, table, table.shape[0], self.k, b.ids,
+                    b.w, b.route_ws, b.route_ws.numel(), stream)
+
     def group(self, b: Buffers, stream=None):
         group_tokens(b.ids, b.T, self.k, self.E, b.counts, b.offsets, b.slot_list, None, 0, stream)
 
@@ -121,6 +126,14 @@ class MoELayer:
     def run_calls(self, x: torch.Tensor, b: Buffers, stream=None):
         """The layer as the four calls in turn."""
         self.route(x, b, stream)
+        self.group(b, stream)
+        self.forward(x, b, stream)
+        self.combine(b, stream)
+        return b.out
+
+    def run_table(self, x: torch.Tensor, b: Buffers, token_ids: torch.Tensor, table: torch.Tensor, stream=None):
+        """The layer with table routing: route_table, then the grouping, experts and combine calls."""
+        self.route_table(x, b, token_ids, table, stream)
         self.group(b, stream)
         self.forward(x, b, stream)
         self.combine(b, stream)

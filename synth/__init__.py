@@ -47,6 +47,7 @@ BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q2SM: 12}
 
 # stream roles (stream id = role << 20 | index)
 _X, _ROUTER, _BIAS, _ZIPF, _HIST, _PPERM, _GATE, _UP, _DOWN = 1, 2, 3, 4, 5, 6, 16, 17, 18
+_TABLE, _TOKID = 7, 8
 W_SIGMA = 0.02
 
 
@@ -203,6 +204,19 @@ def _weights(cfg: Config, seed: int):
     up = _matrices(seed, _UP, cfg.E, cfg.I, cfg.H, cfg.up_fmt)
     down = _matrices(seed, _DOWN, cfg.E, cfg.H, cfg.I, cfg.down_fmt)
     return router, gate, up, down
+
+
+def route_table(seed: int, V: int, E: int, k: int) -> np.ndarray:
+    """A token-id routing table [V, k] int32: row v holds k distinct experts, the first k of a
+    seeded permutation of 0..E-1 drawn for that row (a stand-in for a tokenizer's table)."""
+    return np.stack([permutation(seed, (_TABLE << 20) + v, E)[:k] for v in range(V)]).astype(np.int32)
+
+
+def token_ids(seed: int, T: int, V: int, first: int = 0) -> np.ndarray:
+    """Token ids of tokens first .. first+T-1, uniform over 0..V-1 (a seeded permutation's
+    entries, taken modulo V)."""
+    n = first + T
+    return (permutation(seed, _TOKID << 20, max(n, V))[first:n] % V).astype(np.int32)
 
 
 def tokens(seed: int, T: int, H: int, first: int = 0) -> np.ndarray:

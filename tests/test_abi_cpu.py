@@ -241,3 +241,18 @@ def test_build_scan_flags_dpp_operand_written_too_late():
     assert _dpp_hazards(ok) == []
     other = "v_cvt_f32_i32_e32 v6, v1\n\tv_fmac_f32_dpp v3, v5, v4 row_newbcast:0\n"
     assert _dpp_hazards(other) == []
+
+
+
+def test_table_check_and_route_table_argument_errors():
+    moe.table_check(np.array([[0, 3], [2, 1], [3, 0]], np.int32), 4)
+    for bad in ([[0, 4], [1, 2]], [[0, -1], [1, 2]], [[1, 1], [0, 2]]):
+        with pytest.raises(moe.MoeError) as e:
+            moe.table_check(np.array(bad, np.int32), 4)
+        assert e.value.status == moe.ERR_ARG
+    r = _router()
+    call = lambda **kw: moe.route_table(FAKE, 0, 4, 256, r, None, kw.get("tok", FAKE), kw.get("table", FAKE),
+                                        kw.get("V", 16), 2, FAKE, FAKE, FAKE, 1 << 20, 0)
+    assert _status(lambda: call(table=None)) == moe.ERR_ARG
+    assert _status(lambda: call(tok=None)) == moe.ERR_ARG
+    assert _status(lambda: call(V=0)) == moe.ERR_ARG

@@ -470,3 +470,54 @@ def test_kernel_trace_records_each_launch(torch, name):
     assert tr.count.value == 3 and len(times) == 3
     total = t0.elapsed_time(t1)
     assert all(0.0 < t < total for t in times), (times, total)
+
+
+
+def test_route_table_top_k_rows_match_route(torch):
+    """A device table whose row t is token t's top k from moe_route: moe_route_table returns the
+    same ids and, bit for bit, the same weights."""
+    _say("route_table vs route: cfg3 T=32")
+    wl = synth.make(3, T=32)
+    layer = make_layer(wl)
+    from quantized_moe_routed_amd.layer import act_code
+    x = x_tensor(wl, torch)
+    b = layer.buffers(wl.T, act_code(x))
+    layer.route(x, b)
+    torch.cuda.synchronize()
+    ids, w = b.ids.clone(), b.w.clone()
+    b.ids.zero_()
+    b.w.zero_()
+    layer.route_table(x, b, torch.arange(wl.T, dtype=torch.int32, device="cuda"), ids)
+    torch.cuda.synchronize()
+    assert torch.equal(b.ids, ids)
+    assert torch.equal(b.w.view(torch.int32), w.view(torch.int32))
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_route_table_layer_against_oracle(torch, act):
+    """The layer with table routing (route_table, group, experts, combine) against the oracle's
+    table route, per-slot experts and combine: ids and grouping exact, weights and output within
+    tolerance."""
+    T, H, E, I, k, V = 40, 256, 32, 128, 4, 64
+    _say(f"route_table layer {act}: T={T} E={E} k={k} V={V}")
+    wl = synth.make(synth.custom(T, H, E, I, k, gate_fmt=2, up_fmt=2, down_fmt=1, router_fmt=1, act=act,
+                                 bias="zipf1.1", name=f"table_{act}"))
+    table = synth.route_table(0, V, E, k)
+    tok = synth.token_ids(0, T, V)
+    moe.table_check(table, E)
+    layer = make_layer(wl)
+    from quantized_moe_routed_amd.layer import act_code
+    x = x_tensor(wl, torch)
+    b = layer.buffers(T, act_code(x))
+    layer.run_table(x, b, torch.from_numpy(tok).cuda(), torch.from_numpy(table).cuda())
+    torch.cuda.synchronize()
+    ids, w = oracle.route_table(wl.x, wl.cfg.router_fmt, wl.router[0], wl.bias, tok, table)
+    assert np.array_equal(b.ids.cpu().numpy(), ids)
+    assert_close(b.w.cpu().numpy(), w, "table weights")
+    counts, offsets, slots = oracle.group(ids, E)
+    assert np.array_equal(b.counts.cpu().numpy(), counts)
+    assert np.array_equal(b.slot_list.cpu().numpy()[: T * k], slots)
+    rows = oracle.forward_slots(helpers.fmts(wl), wl.gate, wl.up, wl.down, wl.x, ids, range(T * k))
+    y = np.stack([rows[s] for s in range(T * k)])
+    assert_close(b.y_slot.cpu().numpy()[: T * k], y, "table y_slot")
+    assert_close(b.out.cpu().numpy(), oracle.combine(y, w, ids, None), "table out")

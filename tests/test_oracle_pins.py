@@ -368,3 +368,33 @@ def test_empty_batch():
     assert ids.shape == (0, 2) and w.shape == (0, 2)
     counts, offsets, slots = oracle.group(ids, 8)
     assert counts.sum() == 0 and offsets.tolist() == [0] * 9 and slots.size == 0
+
+
+
+# ---- table routing ---------------------------------------------------------------------------
+def _table_case():
+    wl = synth.make(synth.custom(6, 256, 16, 128, 4, router_fmt=1, bias="zipf1.1", name="table"), experts=False)
+    return wl, oracle.route(wl.x, wl.cfg.router_fmt, wl.router[0], wl.bias, wl.k)
+
+
+def test_route_table_with_top_k_rows_is_the_learned_route():
+    """A table whose row t is token t's learned top k routes exactly as the top k does: the same
+    ids in the same order, the same weights (the C oracle's top-k against the table path)."""
+    wl, (ids, w, _) = _table_case()
+    got_ids, got_w = oracle.route_table(wl.x, wl.cfg.router_fmt, wl.router[0], wl.bias, np.arange(wl.T), ids)
+    assert np.array_equal(got_ids, ids)
+    np.testing.assert_allclose(got_w, w, rtol=1e-6, atol=0)
+
+
+def test_route_table_follows_the_row_and_renormalises():
+    """Reversing every table row reverses ids and weights; the weights of a row sum to 1; a token id
+    picks its row, whatever the token's position."""
+    wl, (ids, _, z) = _table_case()
+    table = np.ascontiguousarray(ids[::-1, ::-1])      # row v = reversed top k of token T-1-v
+    tok = np.arange(wl.T)[::-1].copy()
+    got_ids, got_w = oracle.route_table(wl.x, wl.cfg.router_fmt, wl.router[0], wl.bias, tok, table)
+    assert np.array_equal(got_ids, ids[:, ::-1])
+    np.testing.assert_allclose(got_w.sum(axis=1), 1.0, rtol=1e-6)
+    # the largest logit of a row gets the largest weight
+    for t in range(wl.T):
+        assert int(got_ids[t, np.argmax(got_w[t])]) == int(got_ids[t, np.argmax(z[t, got_ids[t]])])
