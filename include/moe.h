@@ -237,7 +237,7 @@ moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, in
  * were recorded.  The expert kernels (ffn_*) instead hand start[i] and stop[i]
  * to the launch itself (hipExtLaunchKernel), so that they hold the kernel's
  * own start and end, the interval a profiler reports.  Kernel names:
- * route_logits, route_topk, group, prep, front (selection to operands in one
+ * route_logits, route_topk, route_table, group, prep, front (selection to operands in one
  * launch, small batches), ffn_gateup, ffn_down (small tiles),
  * ffn_gateup_large, ffn_down_large, combine.  The caller owns
  * the events and must keep them, and count, alive while tracing; n <= 0
