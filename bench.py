@@ -41,6 +41,7 @@ WORKLOADS = {
     "prefill": 4,
     "ep_share": 5,
     "table_batched": 3,
+    "decode_shared": 2,
 }
 TABLE_V = 8192   # rows of the synthetic token-id routing table
 
@@ -163,6 +164,13 @@ def measure(name, steps, warmup, torch):
     bf16 = wl.cfg.act == "bf16"
     kernel = "ffn_gateup_large" if name == "prefill" else "ffn_gateup"
     run = route = None
+    if name == "decode_shared":
+        # the routed layer, then a Q8_0 shared expert of the routed experts' shapes added to its
+        # output (two gate/up launches a step: the sampled launches 0, 8, 16, ... are the routed ones)
+        import synth
+        from quantized_moe_routed_amd.layer import SharedExpert
+        shared = SharedExpert(H, I, 1, *synth.shared_expert(0, H, I))
+        run = lambda i, b: (layer.run(xs[i], b), shared.add_to(xs[i], b.out))
     if name == "table_batched":
         # table routing: each batch's token ids index a seeded [TABLE_V, k] table of distinct experts
         import synth
@@ -179,6 +187,8 @@ def measure(name, steps, warmup, torch):
     flops = 6.0 * H * I * slots
     # whole-layer bytes: every touched owned expert's weights, the router, x in and the output
     layer_bytes = (d_small + d_large) * per_expert + router_bytes + x_bytes + T * H * 4
+    if name == "decode_shared":
+        layer_bytes += shared.nbytes()
     res = {
         "tokens_per_s": T / (ms * 1e-3),
         "ms_per_step": ms,
@@ -326,10 +336,11 @@ def main():
     wl, head = measure(args.workload, args.steps, args.warmup, torch)
     others = {}
     if not args.only:
-        for name in ("batched_decode", "prefill", "ep_share", "table_batched", "decode"):
+        for name in ("batched_decode", "prefill", "ep_share", "table_batched", "decode_shared", "decode"):
             if name == args.workload:
                 continue
-            steps = {"prefill": 20, "batched_decode": 100, "ep_share": 50, "table_batched": 100, "decode": 200}[name]
+            steps = {"prefill": 20, "batched_decode": 100, "ep_share": 50, "table_batched": 100, "decode_shared": 200,
+                     "decode": 200}[name]
             _, r = measure(name, steps, 5, torch)
             others[name] = r
     T = head["T"]
@@ -343,6 +354,7 @@ def main():
                    "bias, bf16 activations on matrix cores",
         "ep_share": "expert-parallel share: T=128, 128 of 256 experts owned (LPT), H=4096, I=2048, top-8, "
                     "Q2SM gate/up, Q8_0 down, fp32 activations; partial output",
+        "decode_shared": "single-token decode plus a Q8_0 shared expert (I=2048) added to the routed output",
         "table_batched": "batched decode with table routing: T=32, experts from a seeded 8192-row token-id table "
                          "of 8 distinct experts, shapes and formats of batched decode",
     }[args.workload]

@@ -167,6 +167,20 @@ moe_status moe_route_table(const void* x, int32_t xt, int32_t T, int32_t H, cons
                            const float* bias, const int32_t* token_ids, const int32_t* table, int32_t V,
                            int32_t k, int32_t* ids, float* w, void* ws, size_t ws_bytes, hipStream_t s);
 
+/* Shared expert beside the routed sum: out[t] += D(silu(G x_t) * U x_t) for
+ * every token, one fp32 addition per element after the expert's own result
+ * (the pages name a Q8_0 shared expert next to the routed ones but give no
+ * shapes; any format and intermediate size the expert calls take are
+ * accepted).  shared holds exactly one expert (gate/up I x H, down H x I);
+ * out [T, H] fp32 is read and written (call after moe_combine or
+ * moe_layer_forward to add the shared expert to the routed output).  The
+ * expert runs on the same kernels as the routed ones, every token a slot of
+ * the one expert.  Workspace: moe_shared_expert_workspace. */
+moe_status moe_shared_expert_workspace(int32_t T, int32_t H, int32_t I, int32_t xt, size_t* ws_bytes);
+moe_status moe_shared_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, int32_t I,
+                                     const moe_experts* shared, float* out, void* ws, size_t ws_bytes,
+                                     hipStream_t s);
+
 /* Host check of a routing table [V, k] (host memory): every entry in 0..E-1,
  * no expert twice in a row.  MOE_ERR_ARG names the first offending entry. */
 moe_status moe_table_check(const int32_t* table, int32_t V, int32_t k, int32_t E);

@@ -138,6 +138,14 @@ def route_table(x: np.ndarray, router_fmt: int, router: np.ndarray, bias: Option
     return ids.astype(np.int32), w
 
 
+def shared_expert(fmts: Sequence[int], gate: np.ndarray, up: np.ndarray, down: np.ndarray,
+                  x: np.ndarray) -> np.ndarray:
+    """The shared expert's rows [T, H] (fp64): expert() of the one-expert stack on every token (the
+    pages name a shared expert beside the routed ones, antirez/ds4 PR #754, "Supported paths and
+    safety"; the caller adds it to the routed output in fp32)."""
+    return np.stack([expert(fmts, gate[0], up[0], down[0], x[t]) for t in range(x.shape[0])])
+
+
 # ---------------------------------------------------------------- group
 def group(ids: np.ndarray, E: int):
     """Stable grouping of slots s = t*k + j by expert id."""

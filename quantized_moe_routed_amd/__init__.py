@@ -56,6 +56,8 @@ def _load():
     L.moe_route.argtypes = [vp, i32, i32, i32, ctypes.POINTER(QMat), vp, i32, vp, vp, vp, sz, vp]
     L.moe_route_table.argtypes = [vp, i32, i32, i32, ctypes.POINTER(QMat), vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]
     L.moe_table_check.argtypes = [vp, i32, i32, i32]
+    L.moe_shared_expert_workspace.argtypes = [i32, i32, i32, i32, psz]
+    L.moe_shared_expert_forward.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(Experts), vp, vp, sz, vp]
     L.moe_group_tokens.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.moe_expert_forward.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(Experts), vp, i32, i32,
                                      vp, vp, vp, vp, vp, sz, vp]
@@ -71,6 +73,7 @@ def _load():
     L.moe_trace_kernel_every.argtypes = [ctypes.c_char_p, vp, vp, i32, i32, ctypes.POINTER(ctypes.c_int32)]
     for f in ("moe_trace_kernel", "moe_trace_kernel_every", "moe_workspace_size", "moe_route", "moe_group_tokens", "moe_expert_forward", "moe_combine",
               "moe_layer_forward", "moe_route_table", "moe_table_check",
+              "moe_shared_expert_workspace", "moe_shared_expert_forward",
               "moe_planar_bytes", "moe_pack_planar", "moe_place_lpt", "moe_share_tables", "moe_plan_check"):
         getattr(L, f).restype = ctypes.c_int
     return L
@@ -81,7 +84,7 @@ lib = _load()
 EXPORTS = ("moe_last_error", "moe_version", "moe_large_tile_min", "moe_workspace_size", "moe_route", "moe_group_tokens",
            "moe_expert_forward", "moe_combine", "moe_layer_forward", "moe_planar_bytes", "moe_pack_planar", "moe_place_lpt",
            "moe_share_tables", "moe_plan_check", "moe_trace_kernel", "moe_trace_kernel_every", "moe_route_table",
-           "moe_table_check")
+           "moe_table_check", "moe_shared_expert_workspace", "moe_shared_expert_forward")
 
 
 def last_error() -> str:
@@ -231,6 +234,17 @@ class KernelTrace:
 def route_table(x, xt, T, H, router: QMat, bias, token_ids, table, V, k, ids, w, ws, ws_bytes, stream=None):
     _check(lib.moe_route_table(_ptr(x), xt, T, H, ctypes.byref(router), _ptr(bias), _ptr(token_ids), _ptr(table), V,
                                k, _ptr(ids), _ptr(w), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def shared_expert_workspace(T, H, I, xt) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.moe_shared_expert_workspace(T, H, I, xt, ctypes.byref(n)))
+    return n.value
+
+
+def shared_expert_forward(x, xt, T, H, I, shared: Experts, out, ws, ws_bytes, stream=None):
+    _check(lib.moe_shared_expert_forward(_ptr(x), xt, T, H, I, ctypes.byref(shared), _ptr(out), _ptr(ws), ws_bytes,
+                                         _stream(stream)))
 
 
 def table_check(table: np.ndarray, E: int):

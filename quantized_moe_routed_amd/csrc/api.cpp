@@ -463,6 +463,33 @@ hipError_t launch_prep_of(const FwdSetup& f, const void* x, int xt, hipStream_t 
 
 }  // namespace
 
+namespace moe {   // combine.hip
+hipError_t launch_shared_group(int T, int32_t* counts, int32_t* offsets, int32_t* slot_list, hipStream_t s);
+hipError_t launch_add_rows(const float* y, float* out, int64_t n, hipStream_t s);
+}  // namespace moe
+
+// Shared expert workspace: counts [1], offsets [2], slot_list [T], y [T, H] fp32, then the expert
+// forward's own workspace (one expert, one slot per token).
+struct SharedLayout {
+  size_t counts, offsets, slots, y, fwd, total;
+};
+static SharedLayout shared_layout(int T, int H, int I, int xt) {
+  SharedLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  L.counts = take(sizeof(int32_t));
+  L.offsets = take(2 * sizeof(int32_t));
+  L.slots = take((size_t)T * sizeof(int32_t));
+  L.y = take((size_t)T * H * sizeof(float));
+  L.fwd = take(fwd_layout(T, H, I, 1, 1, xt).total);
+  L.total = off;
+  return L;
+}
+
 extern "C" {
 
 moe_status moe_route(const void* x, int32_t xt, int32_t T, int32_t H, const moe_qmat* router, const float* bias,
@@ -742,6 +769,48 @@ moe_status moe_share_tables(const int32_t* owner, int32_t E, int32_t share, cons
     l2g[l] = owned[l];
   }
   *E_local = (int32_t)owned.size();
+  return ok();
+}
+
+moe_status moe_shared_expert_workspace(int32_t T, int32_t H, int32_t I, int32_t xt, size_t* ws_bytes) {
+  if (T < 0 || H <= 0 || I <= 0 || !ws_bytes) return fail(MOE_ERR_ARG, "moe_shared_expert_workspace: bad arguments");
+  *ws_bytes = shared_layout(T, H, I, xt).total;
+  return ok();
+}
+
+moe_status moe_shared_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, int32_t I,
+                                     const moe_experts* shared, float* out, void* ws, size_t ws_bytes, hipStream_t s) {
+  const char* fn = "moe_shared_expert_forward";
+  if (!shared || shared->n_experts != 1) return fail(MOE_ERR_ARG, "%s: shared must hold exactly one expert", fn);
+  if (T < 0 || H <= 0 || I <= 0) return fail(MOE_ERR_ARG, "%s: bad sizes", fn);
+  if (T > 0 && !out) return fail(MOE_ERR_ARG, "%s: out must not be NULL", fn);
+  const SharedLayout L = shared_layout(T, H, I, xt);
+  if (ws_bytes < L.total || (L.total && !ws))
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, L.total);
+  if (!aligned16(ws) || !aligned16(out)) return fail(MOE_ERR_ARG, "%s: workspace and out must be 16-byte aligned", fn);
+  if (T == 0) return ok();
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  int32_t* counts = reinterpret_cast<int32_t*>(b + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  int32_t* slots = reinterpret_cast<int32_t*>(b + L.slots);
+  float* y = reinterpret_cast<float*>(b + L.y);
+  // the argument and device checks of the expert call come first: nothing is launched on failure
+  FwdSetup f;
+  moe_status st = forward_setup(fn, x, xt, T, H, I, 1, shared, nullptr, 1, 1, counts, offsets, slots, y, b + L.fwd,
+                                ws_bytes - L.fwd, s, f);
+  if (st) return st;
+  DevCheck dc;
+  if ((st = stream_device(s, &dc.dev))) return st;
+  dc(out, "out");
+  if (dc.st) return dc.st;
+  hipError_t e = moe::launch_shared_group(T, counts, offsets, slots, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_shared_expert_forward: group launch");
+  e = launch_prep_of(f, x, xt, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_shared_expert_forward: prep launch");
+  e = moe::launch_ffn(f.a, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_shared_expert_forward: FFN launch");
+  e = moe::launch_add_rows(y, out, (int64_t)T * H, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_shared_expert_forward: add launch");
   return ok();
 }
 

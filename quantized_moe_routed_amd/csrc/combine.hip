@@ -2,6 +2,8 @@
 // One thread per (token, 4 columns); each output element is accumulated by a
 // single thread in slot order from +0.0, so the result never depends on
 // scheduling (no atomics anywhere).
+#include <algorithm>
+
 #include "device.h"
 #include "launch.h"
 
@@ -83,6 +85,43 @@ hipError_t launch_combine(const float* y, const float* w, const int32_t* ids, co
   else
     combine_kernel<<<grid, nt, 0, s>>>(y, w, ids, g2l, T, k, H, E, out);
   trace_post("combine", s);
+  return hipGetLastError();
+}
+
+// The shared expert takes every token: one expert with counts = {T}, offsets = {0, T} and the
+// slots in order.
+__global__ __launch_bounds__(256) void shared_group_kernel(int T, int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ slot_list) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < T) slot_list[i] = i;
+  if (i == 0) {
+    counts[0] = T;
+    offsets[0] = 0;
+    offsets[1] = T;
+  }
+}
+
+// out[i] += y[i], one fp32 addition per element (n a multiple of 4).
+__global__ __launch_bounds__(256) void add_rows_kernel(const float4* __restrict__ y, float4* __restrict__ out,
+                                                       int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    const float4 a = out[i], b = y[i];
+    out[i] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+  }
+}
+
+hipError_t launch_shared_group(int T, int32_t* counts, int32_t* offsets, int32_t* slot_list, hipStream_t s) {
+  shared_group_kernel<<<(T + 255) / 256, 256, 0, s>>>(T, counts, offsets, slot_list);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_rows(const float* y, float* out, int64_t n, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 2048);
+  trace_pre("add_shared", s);
+  add_rows_kernel<<<(int)blocks, 256, 0, s>>>(reinterpret_cast<const float4*>(y), reinterpret_cast<float4*>(out), n4);
+  trace_post("add_shared", s);
   return hipGetLastError();
 }
 

@@ -16,7 +16,8 @@ import torch
 
 from . import (ACT_BF16, ACT_F32, W_F32, Experts, combine, expert_forward, group_tokens, layer_forward, pack_planar,
                plan_check,
-               qmat, route, route_table, table_check, workspace_size)
+               qmat, route, route_table, shared_expert_forward, shared_expert_workspace, table_check,
+               workspace_size)
 
 
 def _to_dev(a: Optional[np.ndarray], device) -> Optional[torch.Tensor]:
@@ -156,3 +157,28 @@ def act_code(x: torch.Tensor) -> int:
 
 
 __all__ = ["MoELayer", "DeviceMatrix", "Buffers", "act_code", "W_F32"]
+
+
+class SharedExpert:
+    """The shared expert beside the routed ones: one expert stack (gate/up I x H, down H x I) on one
+    device; add_to(x, out) adds its output to the routed output out in place."""
+
+    def __init__(self, H: int, I: int, fmt: int, gate_aos, up_aos, down_aos, device=None):
+        self.device = torch.device(device or "cuda")
+        self.H, self.I = H, I
+        self.gate = DeviceMatrix(fmt, gate_aos, 1, I, H, self.device)
+        self.up = DeviceMatrix(fmt, up_aos, 1, I, H, self.device)
+        self.down = DeviceMatrix(fmt, down_aos, 1, H, I, self.device)
+        self._experts = Experts(self.gate.qmat(), self.up.qmat(), self.down.qmat(), 1)
+        self._ws = None
+
+    def nbytes(self) -> int:
+        return self.gate.nbytes() + self.up.nbytes() + self.down.nbytes()
+
+    def add_to(self, x: torch.Tensor, out: torch.Tensor, stream=None):
+        T, xt = x.shape[0], act_code(x)
+        n = shared_expert_workspace(T, self.H, self.I, xt)
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = torch.empty(max(n, 1), dtype=torch.uint8, device=self.device)
+        shared_expert_forward(x, xt, T, self.H, self.I, self._experts, out, self._ws, self._ws.numel(), stream)
+        return out

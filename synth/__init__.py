@@ -48,6 +48,7 @@ BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q2SM: 12}
 # stream roles (stream id = role << 20 | index)
 _X, _ROUTER, _BIAS, _ZIPF, _HIST, _PPERM, _GATE, _UP, _DOWN = 1, 2, 3, 4, 5, 6, 16, 17, 18
 _TABLE, _TOKID = 7, 8
+_SGATE, _SUP, _SDOWN = 19, 20, 21
 W_SIGMA = 0.02
 
 
@@ -204,6 +205,13 @@ def _weights(cfg: Config, seed: int):
     up = _matrices(seed, _UP, cfg.E, cfg.I, cfg.H, cfg.up_fmt)
     down = _matrices(seed, _DOWN, cfg.E, cfg.H, cfg.I, cfg.down_fmt)
     return router, gate, up, down
+
+
+def shared_expert(seed: int, H: int, I: int, fmt: int = FMT_Q8_0):
+    """One shared expert (gate, up [1, I, row bytes of H], down [1, H, row bytes of I]) drawn as
+    the routed experts are, N(0, 0.02), in one format (Q8_0 by default)."""
+    return (_matrices(seed, _SGATE, 1, I, H, fmt), _matrices(seed, _SUP, 1, I, H, fmt),
+            _matrices(seed, _SDOWN, 1, H, I, fmt))
 
 
 def route_table(seed: int, V: int, E: int, k: int) -> np.ndarray:

@@ -256,3 +256,13 @@ def test_table_check_and_route_table_argument_errors():
     assert _status(lambda: call(table=None)) == moe.ERR_ARG
     assert _status(lambda: call(tok=None)) == moe.ERR_ARG
     assert _status(lambda: call(V=0)) == moe.ERR_ARG
+
+
+
+def test_shared_expert_argument_errors():
+    assert moe.shared_expert_workspace(4, 256, 128, moe.ACT_F32) > 4 * 256 * 4
+    ex = lambda n: moe.Experts(moe.qmat(moe.W_Q8_0, 128, 256, FAKE, FAKE), moe.qmat(moe.W_Q8_0, 128, 256, FAKE, FAKE),
+                               moe.qmat(moe.W_Q8_0, 256, 128, FAKE, FAKE), n)
+    call = lambda n=1, ws=1 << 24: moe.shared_expert_forward(FAKE, moe.ACT_F32, 4, 256, 128, ex(n), FAKE, FAKE, ws, 0)
+    assert _status(lambda: call(n=2)) == moe.ERR_ARG
+    assert _status(lambda: call(ws=64)) == moe.ERR_WORKSPACE

@@ -521,3 +521,27 @@ def test_route_table_layer_against_oracle(torch, act):
     y = np.stack([rows[s] for s in range(T * k)])
     assert_close(b.y_slot.cpu().numpy()[: T * k], y, "table y_slot")
     assert_close(b.out.cpu().numpy(), oracle.combine(y, w, ids, None), "table out")
+
+
+
+@pytest.mark.parametrize("T,act", [(1, "f32"), (40, "f32"), (300, "f32"), (40, "bf16")])
+def test_shared_expert_adds_to_the_routed_output(torch, T, act):
+    """The layer's routed output plus the shared expert (every token through one Q8_0 expert, on
+    small tiles or, at 300 tokens, large ones) against the oracle's routed output plus its
+    per-token shared expert."""
+    H, E, I, k, Is = 256, 8, 128, 2, 160
+    _say(f"shared expert {act}: T={T} H={H} I_shared={Is}")
+    wl = synth.make(synth.custom(T, H, E, I, k, gate_fmt=2, up_fmt=2, down_fmt=1, router_fmt=1, act=act,
+                                 name=f"shared_{act}"))
+    sg, su, sd = synth.shared_expert(0, H, Is)
+    from quantized_moe_routed_amd.layer import SharedExpert
+    shared = SharedExpert(H, Is, 1, sg, su, sd)
+    layer = make_layer(wl)
+    from quantized_moe_routed_amd.layer import act_code
+    x = x_tensor(wl, torch)
+    b = layer.buffers(T, act_code(x))
+    layer.run(x, b)
+    shared.add_to(x, b.out)
+    torch.cuda.synchronize()
+    ref = oracle_expect(wl)["out"].astype(np.float64) + oracle.shared_expert((1, 1, 1), sg, su, sd, wl.x)
+    assert_close(b.out.cpu().numpy(), ref, f"shared {act} T={T} out")
