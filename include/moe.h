@@ -253,7 +253,7 @@ moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, in
  * own start and end, the interval a profiler reports.  Kernel names:
  * route_logits, route_topk, route_table, group, prep, front (selection to operands in one
  * launch, small batches), ffn_gateup, ffn_down (small tiles),
- * ffn_gateup_large, ffn_down_large, combine.  The caller owns
+ * ffn_gateup_large, ffn_down_large, combine, add_shared.  The caller owns
  * the events and must keep them, and count, alive while tracing; n <= 0
  * switches tracing off. */
 moe_status moe_trace_kernel(const char* name, hipEvent_t* start, hipEvent_t* stop, int32_t n, int32_t* count);
