@@ -15,5 +15,10 @@ def pytest_sessionstart(session):
     # the library is built in-tree; compile it once if nothing is built yet
     lib = os.path.join(ROOT, "quantized_moe_routed_amd", "libmoe.so")
     if not os.path.exists(lib):
-        from quantized_moe_routed_amd import build as _b
-        _b.build()
+        # by file path: the package's __init__ refuses to run without the library
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_moe_build", os.path.join(ROOT, "quantized_moe_routed_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
