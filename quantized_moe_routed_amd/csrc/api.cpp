@@ -105,8 +105,10 @@ size_t route_ws_bytes(int T, int E, int H, int fmt = MOE_W_Q8_0) { return align_
 
 // Expert-forward workspace: tile list, per-token row scales, the fp16
 // activation operand (hi plane; lo plane for fp32 activations) with its block
-// sums, and the intermediate h (hi, lo) with its block sums.  Block-sum rows
-// are padded to a multiple of 32 blocks.
+// sums, the intermediate h in fp32 with its block sums and block maxima, and,
+// where large tiles can occur, the down projection's fp16 hi + lo operand of
+// their rows with its block sums and row scales.  Block rows are padded to a
+// multiple of 32 blocks.
 constexpr int kLargeTile = 128;   // slots per large tile
 
 // Fewest slots of an expert that go to large tiles in a batch of T tokens, 0 = small tiles only.
@@ -138,7 +140,8 @@ TilePlan tile_plan(int T, int H, int I, int k, int E_local, int xt) {
 int pad32(int nb) { return (nb + 31) / 32 * 32; }
 
 struct FwdLayout {
-  size_t n_small, n_large, small, small_tok, large, sigma, xq_hi, xq_lo, sq_hi, sq_lo, h_hi, h_lo, hs_hi, hs_lo, total;
+  size_t n_small, n_large, small, small_tok, large, sigma, xq_hi, xq_lo, sq_hi, sq_lo, h, hs, hm;
+  size_t hq_hi, hq_lo, hsq_hi, hsq_lo, hsig, total;
 };
 
 FwdLayout fwd_layout(int T, int H, int I, int k, int E_local, int xt) {
@@ -162,10 +165,18 @@ FwdLayout fwd_layout(int T, int H, int I, int k, int E_local, int xt) {
   L.xq_lo = xt == MOE_ACT_F32 ? take((size_t)T * H * 2) : 0;
   L.sq_hi = take((size_t)T * nb32H * 2);
   L.sq_lo = take((size_t)T * nb32H * 2);
-  L.h_hi = take(TK * I * 2);
-  L.h_lo = take(TK * I * 2);
-  L.hs_hi = take(TK * nb32I * 2);
-  L.hs_lo = take(TK * nb32I * 2);
+  L.h = take(TK * I * 4);
+  L.hs = take(TK * nb32I * 4);
+  L.hm = take(TK * nb32I * 4);
+  if (tp.max_large > 0 || T == 1) {   // large tiles' operand; one-slot tiles' block-scaled planes
+    L.hq_hi = take(TK * I * 2);
+    L.hq_lo = take(TK * I * 2);
+  }
+  if (tp.max_large > 0) {
+    L.hsq_hi = take(TK * nb32I * 2);
+    L.hsq_lo = take(TK * nb32I * 2);
+    L.hsig = take(TK * sizeof(float));
+  }
   L.total = off;
   return L;
 }
@@ -409,10 +420,19 @@ moe_status forward_setup(const char* fn, const void* x, int32_t xt, int32_t T, i
   a.sq_hi = at16(L.sq_hi);
   a.sq_lo = at16(L.sq_lo);
   a.sigma = reinterpret_cast<const float*>(wsb + L.sigma);
-  a.h_hi = at16(L.h_hi);
-  a.h_lo = at16(L.h_lo);
-  a.hs_hi = at16(L.hs_hi);
-  a.hs_lo = at16(L.hs_lo);
+  auto atf = [&](size_t o) { return reinterpret_cast<float*>(wsb + o); };
+  a.h = atf(L.h);
+  a.hs = atf(L.hs);
+  a.hm = atf(L.hm);
+  if (tp.max_large > 0 || T == 1) {
+    a.hq_hi = at16(L.hq_hi);
+    a.hq_lo = at16(L.hq_lo);
+  }
+  if (tp.max_large > 0) {
+    a.hsq_hi = at16(L.hsq_hi);
+    a.hsq_lo = at16(L.hsq_lo);
+    a.hsig = atf(L.hsig);
+  }
   a.y = y_slot;
   moe::TileLists& tl = f.tl;
   tl = moe::TileLists{};

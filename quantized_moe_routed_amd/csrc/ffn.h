@@ -9,10 +9,14 @@ namespace moe {
 
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 
+constexpr int kMaxFfnK = 8192;      // longest contraction (H or I) the expert kernels take
+
 struct FfnTileArgs {
-  const uint16_t *a_hi, *a_lo;      // activation operand planes, row stride K
-  const uint16_t *s_hi, *s_lo;      // block-sum planes, row stride nb32
-  const float* sigma;               // per-token row scale (gate/up); NULL: kSigmaH (down)
+  const uint16_t *a_hi, *a_lo;      // prepared operand planes, row stride K (gate/up: x; large down: h)
+  const uint16_t *s_hi, *s_lo;      // their block-sum planes, row stride nb32
+  const float* sigma;               // their row scales: per token (gate/up), per grouped position (large down)
+  const float *hf, *hsf, *hmf;      // small down: h, its block sums and block maxima, fp32 and unscaled
+                                    // (row strides K, nb32, nb32), scaled per row while staged
   int K, N, nb32, k;
   QMat w0, w1;                      // gate, up (gate/up) or down (w0 only)
   const int32_t* slot_list;
@@ -22,7 +26,12 @@ struct FfnTileArgs {
   int fd, I, nb32I;                 // gate/up: down format, I, padded block count of h
   int stage_rows;                   // small tiles: rows of the LDS staging area (min(4, T))
   FragConsts kc;
-  uint16_t *h_hi, *h_lo, *hs_hi, *hs_lo;
+  float *h, *hs, *hm;               // gate/up out: h = silu(g) * u (in the operand's K order), its block
+                                    // sums (index order) and block maxima of |h|, row strides I, nb32I, nb32I;
+                                    // one-slot tiles instead write the block-scaled planes below, and in
+                                    // hm the inverse of each block's scale
+  uint16_t *hb_hi, *hb_lo;          // gate/up of one-slot tiles: h as the down projection's fp16 hi + lo
+                                    // operand, each 32-column block at its own power-of-two scale
   float* y;
   SelArgs sel;                      // SEL launches: selection inputs and routing outputs
 };
@@ -65,5 +74,18 @@ __device__ __forceinline__ void wait_vmem_at_most() {
 
 // Large-tile launch (ffn_large.hip): tiles of up to 128 slots of one expert.
 hipError_t launch_large(const FfnTileArgs& t, int fmt, int mode, bool lo, int max_tiles, hipStream_t s);
+
+// The down projection's operand of the rows of the large tiles (ffn_large.hip): each row's h and
+// block sums scaled by the power of two of its largest |h| (row_scale), as fp16 hi + lo planes,
+// and the scale itself.
+struct HConvArgs {
+  const float *h, *hs, *hm;
+  uint16_t *hq_hi, *hq_lo, *hsq_hi, *hsq_lo;
+  float* hsig;
+  const int4* tiles;
+  const int32_t* n_tiles;
+  int I, nb32I;
+};
+hipError_t launch_hconv(const HConvArgs& c, int max_tiles, hipStream_t s);
 
 }  // namespace moe

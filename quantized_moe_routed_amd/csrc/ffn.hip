@@ -19,10 +19,20 @@
 // wave order through LDS, so the result does not depend on scheduling; no
 // atomics.
 //
-// gate/up: h = silu(g) * u for every (slot, column) of the tile, written as
-// the down projection's operand (fp16 hi/lo, in its code order, row scale
-// 2^-6) together with the block sums of h.
-// down:    y_slot[slot][col] = the down projection of h.
+// gate/up: h = silu(g) * u for every (slot, column) of the tile, written in
+// fp32 in the down projection's K order, with the block sum and the largest
+// |h| of each slot's 32 columns.
+// down:    y_slot[slot][col] = the down projection of h.  Tiles of several
+// slots: each wave stages its own range of the tile's h rows, every row scaled
+// by the power of two of its largest |h| (row_scale over the row's block
+// maxima, the rule of the activation operand) and split into the fp16 hi and
+// lo planes, and the row's block sums likewise; the row scale is divided out
+// in the epilogue.  One-slot tiles (single-token batches): gate/up writes each
+// 32-column block of h already as the fp16 hi + lo operand, scaled by the
+// power of two of that block's own largest |h|, with the inverse of that
+// scale and the block's unscaled sum; down stages the planes as they are,
+// multiplies each block's weight scale by the block's inverse factor in the
+// fold, and adds the m-term sum_b m_b S_b on the vector units in fp32.
 #include "device.h"
 #include "fmt.h"
 #include "launch.h"
@@ -50,9 +60,12 @@ __host__ __device__ constexpr size_t one_red_offset(bool sel, int stage_rows, in
   return sel_cand_offset(stage_rows, K, lo) + (sel ? kSelScratchBytes : 0);
 }
 
+
 template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL>
 __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a) {
   constexpr int UB = Codes<F>::kUnitBlocks;
+  constexpr bool CONV = MODE == MODE_DOWN && !ONE;   // down of several slots: converts fp32 h while staging
+  constexpr bool BSC = MODE == MODE_DOWN && ONE;     // down of one slot: block-scaled operand planes
   constexpr int CH = NM == 2 ? 2 : (F == FMT_Q8_0 ? 4 : 1);   // units whose loads are issued together
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ float s_sig[16];
@@ -153,18 +166,61 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   uint16_t* st_hi = reinterpret_cast<uint16_t*>(smem);
   uint16_t* st_lo = st_hi + a.stage_rows * K;
   uint16_t* st_zero = st_lo + (LO ? a.stage_rows * K : 0);   // one row of zeros for rows without a slot
-  if (tid < kStageRows) s_sig[tid] = MODE == MODE_GATEUP && tid < rows ? a.sigma[row_of(tid)] : kSigmaH;
-  {
-    const int k0 = 32 * UB * u_beg, k1 = min(32 * UB * u_end, K);
-    for (int e = k0 + 8 * lane; e < k1; e += 8 * kWave)
-      *reinterpret_cast<uint4*>(st_zero + e) = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (MODE == MODE_GATEUP)
+    if (tid < kStageRows) s_sig[tid] = tid < rows ? a.sigma[row_of(tid)] : 1.0f;
+  const int k0 = 32 * UB * u_beg, k1 = min(32 * UB * u_end, K);
+  for (int e = k0 + 8 * lane; e < k1; e += 8 * kWave)
+    *reinterpret_cast<uint4*>(st_zero + e) = make_uint4(0u, 0u, 0u, 0u);
+  // down: the fp32 h of this wave's range [k0, k1) of every row goes by direct loads into the LDS
+  // bytes that its fp16 pairs will occupy: pass q (values 256 q .. 256 q + n - 1 of the range, n at
+  // most 256) puts its first n / 2 values into the hi plane's bytes of the pass and the rest into
+  // the lo plane's, so that converting a pass reads and writes only that pass's bytes.  The rows'
+  // block maxima come into registers (lane l: row l / LPR, blocks l % LPR + LPR j), ahead of the
+  // weights; once they are in, each wave converts its own range in place, with no barrier.
+  constexpr int LPR = kWave / kStageRows;                 // lanes per row of the block maxima
+  constexpr int HMJ = 64 / LPR;                           // maxima per lane issued early (nb <= 64)
+  [[maybe_unused]] float hmv[HMJ];
+  [[maybe_unused]] int64_t slot_out = 0;                  // down: the output slot of the lane's row
+  // one slot: lane l holds the inverse scale and the sum of block b0 + (l % 32) of the wave's range
+  [[maybe_unused]] float fbl = 1.0f, sbl = 0.0f;
+  if constexpr (MODE == MODE_DOWN) {
+    // the output slot of the row this thread stores in the epilogue
+    // (an opaque zero keeps a one-slot tile's index in a vector register: a uniform value would be
+    // moved to a scalar register right after its load, which would wait for every earlier load)
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    slot_out = a.slot_list[p0 + z + (ONE ? 0 : min(tid >> 4, rows - 1))];
+  }
+  if constexpr (BSC) {
+    const int64_t bi = (int64_t)p0 * a.nb32 + min(k0 / 32 + lane % 32, a.nb32 - 1);
+    fbl = a.hmf[bi];
+    if constexpr (Codes<F>::kHasM) sbl = a.hsf[bi];
+  }
+  if constexpr (CONV) {
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    for (int m = 0; m < rows; ++m)
+      for (int q0 = 0; q0 < k1 - k0; q0 += 4 * kWave) {
+        const int hq = min(4 * kWave, k1 - k0 - q0) / 2;   // values of the pass in each plane
+        if (4 * lane < hq)
+          for (int pl = 0; pl < 2; ++pl) {
+            const float* src = a.hf + (int64_t)(p0 + m) * K + k0 + q0 + pl * hq + 4 * lane;
+            const uint32_t dst = lds0 + (uint32_t)((((pl ? a.stage_rows : 0) + m) * K + k0 + q0) * 2);
+            dma16(src, __builtin_amdgcn_readfirstlane(dst));
+          }
+      }
+    const int mr = lane / LPR;
+    const float* pm = a.hmf + (int64_t)(p0 + (mr < rows ? mr : 0)) * a.nb32 + lane % LPR;
+#pragma unroll
+    for (int j = 0; j < HMJ; ++j) hmv[j] = pm[min(LPR * j, a.nb32 - LPR)];   // (past the row: dropped below)
+  } else {   // gate/up, and one-slot down: the prepared fp16 planes as they are
+
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
     for (int pl = 0; pl < (LO ? 2 : 1); ++pl)
       for (int m = 0; m < rows; ++m)
         for (int c0 = k0; c0 < k1; c0 += 512) {   // 1 KiB per instruction
           const int e = c0 + 8 * lane;
           if (e < k1) {
-            const uint16_t* src = (pl ? a.a_lo : a.a_hi) + (int64_t)row_of(m) * K + e;
+            const uint16_t* src = (pl ? a.a_lo : a.a_hi) + (int64_t)(BSC ? p0 + m : row_of(m)) * K + e;
             const uint32_t dst = lds0 + (uint32_t)((((pl ? a.stage_rows : 0) + m) * K + c0) * 2);
             dma16(src, __builtin_amdgcn_readfirstlane(dst));
           }
@@ -198,19 +254,96 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   const bool svalid = slot_m < rows;
   const uint16_t* ps = (c16 < 8 ? a.s_hi : a.s_lo) + (int64_t)arow * a.nb32;
   // m-term operands of a group of up to 4 of this wave's units (lane group g: unit ug + g): the m
-  // values of the lane's column and the block sums of the slots (rows 0..7 hi, 8..15 lo)
+  // values of the lane's column and the block sums of the slots (rows 0..7 hi, 8..15 lo); down
+  // loads the fp32 sums of h (sraw) and scales and splits them once the row's scale is known
   uint4 sv = zero;
+  [[maybe_unused]] float sraw[8];
+  [[maybe_unused]] bool sin = false;
+  [[maybe_unused]] const float* psf = a.hsf + (int64_t)arow * a.nb32;
   auto load_s = [&](int ug) {
     const int u = ug + g;
-    const uint4 v = *reinterpret_cast<const uint4*>(ps + UB * min(u, n_units - 1));
-    sv = u < u_end && svalid ? v : zero;
+    sin = u < u_end && svalid;
+    if constexpr (BSC) {
+      (void)u;
+    } else if constexpr (CONV) {
+      const float4* p = reinterpret_cast<const float4*>(psf + UB * min(u, n_units - 1));
+      const float4 v0 = p[0], v1 = p[1];
+      sraw[0] = v0.x; sraw[1] = v0.y; sraw[2] = v0.z; sraw[3] = v0.w;
+      sraw[4] = v1.x; sraw[5] = v1.y; sraw[6] = v1.z; sraw[7] = v1.w;
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(ps + UB * min(u, n_units - 1));
+      sv = sin ? v : zero;
+    }
   };
-  if constexpr (Codes<F>::kHasM) load_s(u_beg);
+  [[maybe_unused]] float sig_s = 1.0f;   // down: the scale of the lane's m-term row
+  auto cvt_s = [&]() {
+    if constexpr (CONV) {
+      uint4 hi, lo;
+      split8(sraw, sig_s, hi, lo);
+      sv = sin ? (c16 < 8 ? hi : lo) : zero;
+    }
+  };
+  if constexpr (Codes<F>::kHasM && MODE == MODE_GATEUP) load_s(u_beg);
   load_chunk(u_beg);
+  // nothing that uses a loaded value is scheduled among the loads above: no wait delays their issue
+  __builtin_amdgcn_sched_barrier(0);
   // Every load of this wave is in flight.  Loads complete in issue order, so once no more than the
   // chunk's code and scale loads (issued last) are outstanding, the slices are in LDS and the m-term operands in registers; the codes
   // themselves are waited for where they are used.
   wait_vmem_at_most<CH * kNT * NM * 2>();
+  // down: every row's scale from its block maxima, then this wave's range of each row converted in
+  // place, four (row, pass) items per lane at a time: each item's values are read before any of
+  // its pairs is written (a wave's LDS operations take effect in order)
+  [[maybe_unused]] float sig = 1.0f;   // the scale of row lane / LPR
+  if constexpr (CONV) {
+    const int mr = lane / LPR;
+    float hmx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < HMJ; ++j) hmx = fmaxf(hmx, LPR * j + lane % LPR < nb ? hmv[j] : 0.0f);
+    if (nb > 64)   // rows past 2048 values: the other maxima now (this waits for every load)
+      for (int b = 64 + lane % LPR; b < nb; b += LPR)
+        hmx = fmaxf(hmx, a.hmf[(int64_t)(p0 + (mr < rows ? mr : 0)) * a.nb32 + b]);
+    if (mr >= rows) hmx = 0.0f;
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) hmx = fmaxf(hmx, __shfl_xor(hmx, o, kWave));
+    sig = row_scale(hmx);
+    constexpr int IB = 2;   // rows converted together
+    for (int m0 = 0; m0 < rows; m0 += IB)
+      for (int q0 = 0; q0 < k1 - k0; q0 += 4 * kWave) {
+        const int hq = min(4 * kWave, k1 - k0 - q0) / 2, j = 4 * lane;
+        const bool act = j < 2 * hq;
+        // the lane's four values of the pass (row 0): the hi plane's bytes hold the first hq
+        const float* src = j < hq ? reinterpret_cast<const float*>(st_hi + k0 + q0) + j
+                                  : reinterpret_cast<const float*>(st_lo + k0 + q0) + (j - hq);
+        float4 v[IB];
+#pragma unroll
+        for (int i = 0; i < IB; ++i)
+          if (act) v[i] = *reinterpret_cast<const float4*>(src + (min(m0 + i, rows - 1) * K) / 2);
+#pragma unroll
+        for (int i = 0; i < IB; ++i) {
+          const int m = m0 + i;
+          const float sc =
+              __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(sig), (m * LPR) % kWave)) * 64.0f;
+          if (act && m < rows) {
+            uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+            split_f16(v[i].x * sc, h0, l0);
+            split_f16(v[i].y * sc, h1, l1);
+            split_f16(v[i].z * sc, h2, l2);
+            split_f16(v[i].w * sc, h3, l3);
+            *reinterpret_cast<uint2*>(st_hi + m * K + k0 + q0 + j) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+            *reinterpret_cast<uint2*>(st_lo + m * K + k0 + q0 + j) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+          }
+        }
+      }
+    if constexpr (Codes<F>::kHasM) {
+      // the first group's block sums, issued now (after the weights, which the main loop waits for
+      // right away), so that they are not held in registers through the conversion
+      sig_s = __shfl(sig, (slot_m < rows ? slot_m : 0) * LPR % kWave, kWave);
+      load_s(u_beg);
+      wait_vmem();
+      cvt_s();
+    }
+  }
   f32x4_t acc[kNT][NM];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt)
@@ -219,13 +352,35 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
 
   // m-term (2-bit blocks only): sum_b m_b (sigma S_b) over the wave's own units, four units (32
   // blocks) per product, the first group before the main loop
-  auto mterm = [&]() {
+  // (one slot: on the vector units in fp32, sum_b m_b S_b for unit ug + g in lane group g, the
+  // block sums read by lane index from sbl, in block order; the groups are added after the loop)
+  [[maybe_unused]] float mtacc[kNT] = {};
+  auto mterm = [&](int ug) {
+    if constexpr (BSC) {
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
+      for (int gg = 0; gg < 4; ++gg) {
+        if (ug + gg >= u_end) break;
 #pragma unroll
-      for (int mt = 0; mt < NM; ++mt) acc[nt][mt] = mfma16(sv, mv[nt][mt], acc[nt][mt]);   // sigma * value units
+        for (int nt = 0; nt < kNT; ++nt) {
+          const uint32_t mw[4] = {mv[nt][0].x, mv[nt][0].y, mv[nt][0].z, mv[nt][0].w};
+          float t = 0.0f;
+#pragma unroll
+          for (int i = 0; i < UB; ++i) {
+            const float sb = __uint_as_float(
+                (uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(sbl), (ug + gg - u_beg) * UB + i));
+            t = fmaf(half_bits_to_float((i & 1) ? (mw[i >> 1] >> 16) : (mw[i >> 1] & 0xFFFFu)), sb, t);
+          }
+          mtacc[nt] += g == gg ? t : 0.0f;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < NM; ++mt) acc[nt][mt] = mfma16(sv, mv[nt][mt], acc[nt][mt]);   // sigma * value units
+    }
   };
-  if constexpr (Codes<F>::kHasM) mterm();
+  if constexpr (Codes<F>::kHasM) mterm(u_beg);
 
   // main loop over this wave's code units, a unit as soon as its codes are in; activations from LDS
   for (int u0 = u_beg; u0 < u_end; u0 += CH) {
@@ -239,6 +394,10 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
         const int b = u * UB + i;
         if (b >= nb) break;
         const uint4 av = *reinterpret_cast<const uint4*>(pa + 32 * b);
+        // one slot: the block's inverse operand scale, folded into its weight scales
+        [[maybe_unused]] float fb = 1.0f;
+        if constexpr (BSC)
+          fb = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(fbl), (u - u_beg) * UB + i));
         // per output tile: the fragments of both matrices, both products, then both folds, so
         // that no fold waits on the product issued just before it
 #pragma unroll
@@ -252,6 +411,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
 #pragma unroll
           for (int mt = 0; mt < NM; ++mt) {
             float d = d_of<F>(dw[j][nt][mt], i);
+            if constexpr (BSC) d *= fb;   // (a power of two: exact)
             // several slots: convert the scale once, then plain fp32 FMAs (one slot: a single
             // mixed-precision FMA is cheaper)
             if (!ONE) asm volatile("" : "+v"(d));
@@ -271,7 +431,17 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
     for (int ug = u_beg + 4; ug < u_end; ug += 4) {
       load_m(ug);
       load_s(ug);
-      mterm();
+      cvt_s();
+      mterm(ug);
+    }
+    if constexpr (BSC) {
+      // the lane groups' sums of each column, added in group order, join row 0 (lanes 0 .. 15)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        float t = mtacc[nt] + __shfl_xor(mtacc[nt], 16, kWave);
+        t += __shfl_xor(t, 32, kWave);
+        if (lane < 16) acc[nt][0][0] += t;
+      }
     }
   }
   if constexpr (ONE) {
@@ -297,8 +467,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
       float v = R1(0, 0);
 #pragma unroll
       for (int w = 1; w < kFfnWaves; ++w) v += R1(w, 0);
-      const int64_t slot = a.slot_list[p0];
-      a.y[slot * a.N + n0 + 16 * nt + l] = v * (1.0f / kSigmaH);
+      a.y[slot_out * a.N + n0 + 16 * nt + l] = v * (1.0f / sig);   // a power of two: exact
     } else {
       float gs = R1(0, 0), us = R1(0, 1);
 #pragma unroll
@@ -310,27 +479,30 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
       const float h = silu(gs * inv) * (us * inv);
       const int col = n0 + lane;
       const int blk = col >> 5, kk = col & 31, gg = kk >> 3;
-      uint32_t hi, lo;
-      split_f16(h, hi, lo);   // h * kSigmaH * 2^6
-      const int64_t at = (int64_t)p0 * a.I + 32 * blk + 8 * gg + frag_val(kk & 7);
-      a.h_hi[at] = (uint16_t)hi;
-      a.h_lo[at] = (uint16_t)lo;
-      // block sum of h over the tile's 32 columns, in index order
-      float sacc = 0.0f;
+      // block sum of h over the tile's 32 columns, in index order, and their largest |h|
+      float sacc = 0.0f, smax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16 * kNT; ++i) sacc += __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(h), i));
+      for (int i = 0; i < 16 * kNT; ++i) {
+        const float hi = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(h), i));
+        sacc += hi;
+        smax = fmaxf(smax, fabsf(hi));
+      }
+      // the down projection's operand of this block: h times 2^6 and the block's own scale, as an
+      // fp16 hi + lo pair; with it the inverse of the scale and the block's unscaled sum
+      const float sb = row_scale(smax);
+      uint32_t hi, lo;
+      split_f16(h * sb * 64.0f, hi, lo);
+      const int64_t at = (int64_t)p0 * a.I + 32 * blk + 8 * gg + frag_val(kk & 7);
+      a.hb_hi[at] = (uint16_t)hi;
+      a.hb_lo[at] = (uint16_t)lo;
       if (lane == 0) {
-        split_f16(sacc * kSigmaH, hi, lo);
         const int64_t at_s = (int64_t)p0 * a.nb32I + n0 / 32;
-        a.hs_hi[at_s] = (uint16_t)hi;
-        a.hs_lo[at_s] = (uint16_t)lo;
+        a.hs[at_s] = sacc;
+        a.hm[at_s] = 1.0f / sb;
       }
       if (blockIdx.x == 0) {
         const int nbI = a.I / 32;
-        for (int bb = nbI + lane; bb < a.nb32I; bb += 16 * kNT) {
-          a.hs_hi[(int64_t)p0 * a.nb32I + bb] = 0;
-          a.hs_lo[(int64_t)p0 * a.nb32I + bb] = 0;
-        }
+        for (int bb = nbI + lane; bb < a.nb32I; bb += 16 * kNT) a.hs[(int64_t)p0 * a.nb32I + bb] = 0.0f;
       }
     }
     return;
@@ -355,14 +527,14 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   const bool owner = tid < 16 * kStageRows;
   const int lhi = 16 * ((m >> 2) & 1) + l, llo = lhi + 32, cm = m & 3;
   if constexpr (MODE == MODE_DOWN) {
+    const float inv = 1.0f / __shfl(sig, (m & 7) * (kWave / kStageRows), kWave);   // a power of two: exact
     if (owner && m < rows) {
-      const int64_t slot = a.slot_list[p0 + m];
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
         float v = R(0, nt, 0, cm, lhi) + R(0, nt, 0, cm, llo);
 #pragma unroll
         for (int w = 1; w < kFfnWaves; ++w) v += R(w, nt, 0, cm, lhi) + R(w, nt, 0, cm, llo);
-        a.y[slot * a.N + n0 + 16 * nt + l] = v * (1.0f / kSigmaH);
+        a.y[slot_out * a.N + n0 + 16 * nt + l] = v * inv;
       }
     }
   } else {
@@ -382,36 +554,28 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
         h = silu(gs * inv) * (us * inv);
         const int col = n0 + cl;
         const int blk = col >> 5, kk = col & 31, gg = kk >> 3;
-        const int e = frag_val(kk & 7);
-        uint32_t hi, lo;
-        split_f16(h, hi, lo);   // h * kSigmaH * 2^6
-        const int64_t at = (int64_t)(p0 + m) * a.I + 32 * blk + 8 * gg + e;
-        a.h_hi[at] = (uint16_t)hi;
-        a.h_lo[at] = (uint16_t)lo;
+        a.h[(int64_t)(p0 + m) * a.I + 32 * blk + 8 * gg + frag_val(kk & 7)] = h;
       }
       if (owner) hbuf[m * 33 + cl] = h;
     }
     __syncthreads();
-    // block sum of h over this tile's 32 columns (index order), and the zero padding
-    if (tid < 16) {
-      if (tid < rows) {
-        float sacc = 0.0f;
-        for (int i = 0; i < 32; ++i) sacc += hbuf[tid * 33 + i];
-        uint32_t hi, lo;
-        split_f16(sacc * kSigmaH, hi, lo);
-        const int64_t at = (int64_t)(p0 + tid) * a.nb32I + n0 / 32;
-        a.hs_hi[at] = (uint16_t)hi;
-        a.hs_lo[at] = (uint16_t)lo;
+    // block sum of h over this tile's 32 columns (index order) and their largest |h|, and the
+    // zero padding of the block sums
+    if (tid < rows) {
+      float sacc = 0.0f, smax = 0.0f;
+      for (int i = 0; i < 32; ++i) {
+        sacc += hbuf[tid * 33 + i];
+        smax = fmaxf(smax, fabsf(hbuf[tid * 33 + i]));
       }
+      const int64_t at = (int64_t)(p0 + tid) * a.nb32I + n0 / 32;
+      a.hs[at] = sacc;
+      a.hm[at] = smax;
     }
     if (blockIdx.x == 0) {
       const int nbI = a.I / 32;
       for (int j = tid; j < 16 * (a.nb32I - nbI); j += kFfnThreads) {
         const int mm = j % 16, bb = nbI + j / 16;
-        if (mm < rows) {
-          a.hs_hi[(int64_t)(p0 + mm) * a.nb32I + bb] = 0;
-          a.hs_lo[(int64_t)(p0 + mm) * a.nb32I + bb] = 0;
-        }
+        if (mm < rows) a.hs[(int64_t)(p0 + mm) * a.nb32I + bb] = 0.0f;
       }
     }
   }
@@ -427,6 +591,7 @@ static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_
     const size_t one = one_red_offset(SEL, t.stage_rows, t.K, LO) + (size_t)kFfnWaves * kNT * NM * 16 * 4;
     if (lds < one) lds = one;
   }
+
   auto kern = ffn_small_kernel<F, NM, LO, MODE, ONE, SEL>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -454,7 +619,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   t.a_hi = a.xq_hi; t.a_lo = a.xq_lo; t.s_hi = a.sq_hi; t.s_lo = a.sq_lo; t.sigma = a.sigma;
   t.K = a.H; t.N = a.I; t.nb32 = a.nb32H; t.w0 = a.gate; t.w1 = a.up;
   t.fd = a.fd; t.I = a.I; t.nb32I = a.nb32I;
-  t.h_hi = a.h_hi; t.h_lo = a.h_lo; t.hs_hi = a.hs_hi; t.hs_lo = a.hs_lo;
+  t.h = a.h; t.hs = a.hs; t.hm = a.hm; t.hb_hi = a.hq_hi; t.hb_lo = a.hq_lo;
   const bool lo = a.xq_lo != nullptr;
   const bool one = a.T == 1;
 #define MOE_SMALL(F, NM, LO, MODE) \
@@ -482,8 +647,18 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
     trace_post("ffn_gateup_large", s);
     if (err != hipSuccess) return err;
   }
-  // down: h (hi + lo) x down  ->  y_slot
-  t.a_hi = a.h_hi; t.a_lo = a.h_lo; t.s_hi = a.hs_hi; t.s_lo = a.hs_lo; t.sigma = nullptr;
+  // the large tiles' rows of h as the down projection's prepared operand
+  if (a.max_large > 0) {
+    const HConvArgs c{a.h, a.hs, a.hm, a.hq_hi, a.hq_lo, a.hsq_hi, a.hsq_lo, a.hsig, a.large, a.n_large, a.I,
+                      a.nb32I};
+    trace_pre("hconv", s);
+    err = launch_hconv(c, a.max_large, s);
+    trace_post("hconv", s);
+    if (err != hipSuccess) return err;
+  }
+  // down: h (hi + lo) x down  ->  y_slot; small tiles scale and split their rows of h themselves
+  t.a_hi = a.hq_hi; t.a_lo = a.hq_lo; t.s_hi = a.hsq_hi; t.s_lo = a.hsq_lo; t.sigma = a.hsig;
+  t.hf = a.h; t.hsf = a.hs; t.hmf = a.hm;
   t.K = a.I; t.N = a.H; t.nb32 = a.nb32I; t.w0 = a.down; t.w1 = a.down;
   t.y = a.y;
   t.tiles = a.small; t.n_tiles = a.n_small;

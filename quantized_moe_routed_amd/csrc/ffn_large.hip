@@ -25,8 +25,11 @@
 //   * Workgroups are numbered so that the column tiles of one slot tile are
 //     consecutive on one XCD (workgroup i runs on XCD i mod 8): the tile's
 //     activation rows are fetched from memory once per XCD L2.
-// The epilogues are those of the small-tile kernel: h = silu(g) * u written as
-// the down projection's operand with its block sums, or y_slot = 2^6 acc.
+// The epilogues are those of the small-tile kernel: h = silu(g) * u in fp32
+// with its block sums and block maxima, or y_slot = acc / sigma of the row.
+// The down projection's operand of the large tiles' rows is prepared between
+// the two projections by hconv_kernel (below): each row of h scaled by the
+// power of two of its largest |h| and split into fp16 hi and lo planes.
 #include "device.h"
 #include "fmt.h"
 #include "launch.h"
@@ -425,7 +428,7 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
           const int64_t slot = s_slot[row];
 #pragma unroll
           for (int nt = 0; nt < NT2; ++nt)
-            if (colv[nt]) a.y[slot * N + n0 + 32 * nt + c32] = acc[mi][nt][0][e] * (1.0f / kSigmaH);
+            if (colv[nt]) a.y[slot * N + n0 + 32 * nt + c32] = acc[mi][nt][0][e] * s_inv[row];
         }
       } else {
         // NT2 == 1: the wave's 32 columns are exactly block n0 / 32 of h
@@ -433,23 +436,19 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
         if (valid && colv[0]) {
           const float inv = s_inv[row];
           h = silu(acc[mi][0][0][e] * inv) * (acc[mi][0][1][e] * inv);
-          const int el = frag_val(c32 & 7);
-          uint32_t hi, lo;
-          split_f16(h, hi, lo);   // h * kSigmaH * 2^6
-          const int64_t at = (int64_t)(p0 + row) * a.I + n0 + 8 * (c32 >> 3) + el;
-          a.h_hi[at] = (uint16_t)hi;
-          a.h_lo[at] = (uint16_t)lo;
+          a.h[(int64_t)(p0 + row) * a.I + n0 + 8 * (c32 >> 3) + frag_val(c32 & 7)] = h;
         }
-        // block sum over the 32 lanes of this row (fixed order)
-        float hs = h;
+        // block sum over the 32 lanes of this row (fixed order) and the block's largest |h|
+        float hs = h, hm = fabsf(h);
 #pragma unroll
-        for (int m = 1; m < 32; m <<= 1) hs += __shfl_xor(hs, m, kWave);
+        for (int m = 1; m < 32; m <<= 1) {
+          hs += __shfl_xor(hs, m, kWave);
+          hm = fmaxf(hm, __shfl_xor(hm, m, kWave));
+        }
         if (valid && colv[0] && c32 == 0) {
-          uint32_t hi, lo;
-          split_f16(hs * kSigmaH, hi, lo);
           const int64_t at = (int64_t)(p0 + row) * a.nb32I + n0 / 32;
-          a.hs_hi[at] = (uint16_t)hi;
-          a.hs_lo[at] = (uint16_t)lo;
+          a.hs[at] = hs;
+          a.hm[at] = hm;
         }
       }
     }
@@ -458,10 +457,7 @@ __device__ __forceinline__ void large_tile(const FfnTileArgs& a, int le, int p0,
     const int nbI = a.I / 32, npad = a.nb32I - nbI;
     for (int j = lane; j < kLgRows * npad; j += kWave) {
       const int row = j % kLgRows, bb = nbI + j / kLgRows;
-      if (row < rows) {
-        a.hs_hi[(int64_t)(p0 + row) * a.nb32I + bb] = 0;
-        a.hs_lo[(int64_t)(p0 + row) * a.nb32I + bb] = 0;
-      }
+      if (row < rows) a.hs[(int64_t)(p0 + row) * a.nb32I + bb] = 0.0f;
     }
   }
 }
@@ -475,15 +471,17 @@ __global__ __launch_bounds__((LargeCfg<F, NM, LO, MODE, NT2, WM, CG>::THREADS), 
   const int tile = (id & 7) + 8 * (q / n_ct), ct = q % n_ct;
   if (tile >= *a.n_tiles) return;   // the whole workgroup
   const int4 tl = a.tiles[tile];
-  // per-row slot and inverse row scale of the tile, for the m-term and the epilogue; written by
-  // the first 128 threads, made visible by the first stage barrier inside the tile loop
+  // per-row slot and inverse row scale of the tile (the token's, or that of the row of h), for the
+  // m-term and the epilogue; written by the first 128 threads, made visible by the first stage
+  // barrier inside the tile loop
   __shared__ int32_t s_slot[kLgRows];
   __shared__ float s_inv[kLgRows];
   if (threadIdx.x < kLgRows) {
     const int r = (int)threadIdx.x < tl.z ? (int)threadIdx.x : 0;
     const int32_t sl = a.slot_list[tl.y + r];
     s_slot[threadIdx.x] = sl;
-    s_inv[threadIdx.x] = MODE == MODE_GATEUP ? 1.0f / a.sigma[sl / a.k] : 1.0f;   // a power of two: exact
+    // a power of two: exact
+    s_inv[threadIdx.x] = 1.0f / (MODE == MODE_GATEUP ? a.sigma[sl / a.k] : a.sigma[tl.y + r]);
   }
   const int wm = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) / CG;
   int r0 = wm * 32 * C::MIMAX;
@@ -523,6 +521,48 @@ static hipError_t launch_large_t(const FfnTileArgs& t, int max_tiles, hipStream_
   const int n_ct = (t.N + C::BN - 1) / C::BN;
   const int grid = 8 * n_ct * ((max_tiles + 7) / 8);
   return launch_stamped(ffn_large_kernel<F, NM, LO, MODE, NT2, WM, CG>, dim3(grid), dim3(C::THREADS), lds, s, t, n_ct);
+}
+
+// The down projection's operand of the rows of the large tiles.  Workgroup (tile, q) takes rows
+// 8 q .. 8 q + 7 of the tile, a wave per row: the row's scale from its block maxima (row_scale, the
+// rule of the activation operand), then h times 2^6 sigma and the block sums times sigma as fp16
+// hi + lo pairs.  Each row is read and written once.
+constexpr int kConvWaves = 8;
+
+__global__ __launch_bounds__(kConvWaves * kWave) void hconv_kernel(HConvArgs c) {
+  const int tile = blockIdx.x;
+  if (tile >= *c.n_tiles) return;
+  const int4 tl = c.tiles[tile];
+  const int r = blockIdx.y * kConvWaves + (int)(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+  if (r >= tl.z) return;   // the whole wave
+  const int64_t p = tl.y + r;
+  const int nb = c.I / 32;
+  float m = 0.0f;
+  for (int b = lane; b < nb; b += kWave) m = fmaxf(m, c.hm[p * c.nb32I + b]);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  const float sg = row_scale(m);
+  if (lane == 0) c.hsig[p] = sg;
+  for (int ch = lane; ch < c.I / 8; ch += kWave) {
+    const float4* src = reinterpret_cast<const float4*>(c.h + p * c.I + 8 * ch);
+    const float4 v0 = src[0], v1 = src[1];
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint4 hi, lo;
+    split8(v, sg * 64.0f, hi, lo);
+    *reinterpret_cast<uint4*>(c.hq_hi + p * c.I + 8 * ch) = hi;
+    *reinterpret_cast<uint4*>(c.hq_lo + p * c.I + 8 * ch) = lo;
+  }
+  for (int b = lane; b < c.nb32I; b += kWave) {   // (the padding blocks hold zeros)
+    uint32_t hi, lo;
+    split_f16(c.hs[p * c.nb32I + b] * sg, hi, lo);
+    c.hsq_hi[p * c.nb32I + b] = (uint16_t)hi;
+    c.hsq_lo[p * c.nb32I + b] = (uint16_t)lo;
+  }
+}
+
+hipError_t launch_hconv(const HConvArgs& c, int max_tiles, hipStream_t s) {
+  hconv_kernel<<<dim3(max_tiles, kLgRows / kConvWaves), kConvWaves * kWave, 0, s>>>(c);
+  return hipGetLastError();
 }
 
 // Two row groups of waves (8 waves, two per SIMD): each wave holds half the accumulators, and

@@ -62,7 +62,26 @@ __device__ __forceinline__ void split_f16(float v, uint32_t& hi, uint32_t& lo) {
   lo = f16_bits(v - (float)h);
 }
 
-constexpr float kSigmaH = 0.015625f;  // 2^-6: row scale of the intermediate h
+// Power-of-two scale of an operand row whose largest magnitude is m: sigma = 2^(9 - E), E the
+// smallest integer with m < 2^E (E = 0 for an all-zero row), so that every value times
+// sigma * 2^6 lies below 2^15 and its block sums times sigma below 2^14.  A value within 2^18 of
+// the row's largest then keeps a normal fp16 lo half, i.e. 22 significant bits in its hi + lo
+// pair; smaller ones keep an absolute error below 2^-25 in these units (2^-39 of the largest).  E
+// is kept at -110 or above so that sigma stays a finite fp32 number for subnormal rows.
+__device__ __forceinline__ float row_scale(float m) {
+  int ex = 0;
+  if (m > 0.0f) (void)frexpf(m, &ex);   // m = f * 2^ex, f in [0.5, 1): m < 2^ex
+  return ldexpf(1.0f, 9 - max(ex, -110));
+}
+
+// hi + lo fp16 pairs of 8 values times sc, packed in the order given
+__device__ __forceinline__ void split8(const float (&v)[8], float sc, uint4& hi, uint4& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) split_f16(v[e] * sc, h[e], l[e]);
+  hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+  lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+}
 
 template <int FMT>
 struct Codes;

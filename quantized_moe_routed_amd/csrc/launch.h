@@ -94,7 +94,9 @@ struct FfnArgs {
   int bm_small;               // slots per small tile (4 or 8)
   const uint16_t *xq_hi, *xq_lo, *sq_hi, *sq_lo;
   const float* sigma;
-  uint16_t *h_hi, *h_lo, *hs_hi, *hs_lo;
+  float *h, *hs, *hm;           // h = silu(g) * u, its block sums and block maxima (fp32, unscaled)
+  uint16_t *hq_hi, *hq_lo, *hsq_hi, *hsq_lo;   // large tiles: the down projection's operand of their rows
+  float* hsig;                  //   and its row scales (NULL when no large tiles can exist)
   float* y;
   // non-NULL: the gate/up launch selects, groups and numbers the small tiles itself from finished
   // logits (batches of at most kSelMaxTokens tokens, no large tiles) and stores the routing

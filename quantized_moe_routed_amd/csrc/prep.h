@@ -3,8 +3,8 @@
 // batches).
 //
 // Activation operand of token t (see fmt.h):
-//   sigma_t = 2^(9-E), E the smallest integer with max_i |x[t,i]| < 2^E
-//             (1 for an all-zero token), so that |x| * sigma * 2^6 < 2^15;
+//   sigma_t = row_scale(max_i |x[t,i]|) = 2^(9-E), E the smallest integer with
+//             max_i |x[t,i]| < 2^E (fmt.h), so that |x| * sigma * 2^6 < 2^15;
 //   A'[t][32b+8g+e] = x[t][32b+8g+frag_val(e)] * sigma_t * 2^6        (hi, lo)
 //   S'[t][b]        = sigma_t * sum_{i<32} x[t][32b+i]               (hi, lo)
 // The block sums are taken in index order in fp32; blocks past H/32 up to
@@ -77,9 +77,7 @@ __device__ void prep_token(const void* __restrict__ x, int t, int H, int nb32, u
   float m = 0.0f;
 #pragma unroll
   for (int w = 0; w < NT / kWave; ++w) m = fmaxf(m, wmax[w]);
-  int ex = 0;
-  if (m > 0.0f) (void)frexpf(m, &ex);   // m = f * 2^ex, f in [0.5, 1): m < 2^ex
-  const float sg = ldexpf(1.0f, 9 - ex);
+  const float sg = row_scale(m);
   if (tid == 0) sigma[t] = sg;
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {

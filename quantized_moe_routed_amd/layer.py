@@ -170,15 +170,26 @@ class SharedExpert:
         self.up = DeviceMatrix(fmt, up_aos, 1, I, H, self.device)
         self.down = DeviceMatrix(fmt, down_aos, 1, H, I, self.device)
         self._experts = Experts(self.gate.qmat(), self.up.qmat(), self.down.qmat(), 1)
-        self._ws = None
+        self._ws = {}   # one workspace per stream handle
 
     def nbytes(self) -> int:
         return self.gate.nbytes() + self.up.nbytes() + self.down.nbytes()
 
     def add_to(self, x: torch.Tensor, out: torch.Tensor, stream=None):
+        """out += the shared expert of x, on `stream` (a torch stream or a raw handle; None: the
+        current stream).  Each stream gets its own workspace, recorded on that stream, so a regrown
+        workspace is not handed out again while the stream's earlier calls may still use it."""
         T, xt = x.shape[0], act_code(x)
         n = shared_expert_workspace(T, self.H, self.I, xt)
-        if self._ws is None or self._ws.numel() < n:
-            self._ws = torch.empty(max(n, 1), dtype=torch.uint8, device=self.device)
-        shared_expert_forward(x, xt, T, self.H, self.I, self._experts, out, self._ws, self._ws.numel(), stream)
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        elif isinstance(stream, int):
+            stream = torch.cuda.ExternalStream(stream, device=self.device)
+        key = stream.cuda_stream
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < n:
+            ws = torch.empty(max(n, 1), dtype=torch.uint8, device=self.device)
+            ws.record_stream(stream)
+            self._ws[key] = ws
+        shared_expert_forward(x, xt, T, self.H, self.I, self._experts, out, ws, ws.numel(), stream)
         return out

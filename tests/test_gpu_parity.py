@@ -12,7 +12,7 @@ import synth
 import quantized_moe_routed_amd as moe
 import helpers
 from helpers import assert_close, oracle_expect, sha
-from gpu_util import make_layer, run, torch_mod, x_tensor
+from gpu_util import check_against_oracle, make_layer, run, torch_mod, x_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -20,25 +20,6 @@ pytestmark = pytest.mark.gpu
 def _say(msg):
     print(f"[gpu-parity] {msg}", flush=True)
     sys.stdout.flush()
-
-
-def check_against_oracle(wl, got, ref, slots_checked=None, what=""):
-    T, k = wl.T, wl.k
-    tok = ref["tokens"]
-    assert np.array_equal(got["ids"][tok], ref["ids"]), f"{what}: expert ids differ"
-    assert_close(got["w"][tok], ref["w"], f"{what} weights")
-    if len(tok) == T:
-        counts, offsets, slots = oracle.group(ref["ids"], wl.E)
-        assert np.array_equal(got["counts"], counts), f"{what}: counts differ"
-        assert np.array_equal(got["offsets"], offsets), f"{what}: offsets differ"
-        assert np.array_equal(got["slot_list"], slots), f"{what}: slot_list differs"
-    # y rows of the checked tokens' (owned) slots
-    rows = np.concatenate([np.arange(t * k, (t + 1) * k) for t in tok])
-    ref_y = ref["y"]
-    owned = ~np.isnan(ref_y[:, 0])
-    if owned.any():
-        assert_close(got["y"][rows][owned], ref_y[owned], f"{what} y_slot")
-    assert_close(got["out"][tok], ref["out"], f"{what} out")
 
 
 @pytest.fixture(scope="module")
@@ -524,18 +505,20 @@ def test_route_table_layer_against_oracle(torch, act):
 
 
 
-@pytest.mark.parametrize("T,act", [(1, "f32"), (40, "f32"), (300, "f32"), (40, "bf16")])
-def test_shared_expert_adds_to_the_routed_output(torch, T, act):
-    """The layer's routed output plus the shared expert (every token through one Q8_0 expert, on
-    small tiles or, at 300 tokens, large ones) against the oracle's routed output plus its
-    per-token shared expert."""
+@pytest.mark.parametrize("T,act,sfmt", [(1, "f32", 1), (8, "f32", 1), (32, "f32", 1), (40, "f32", 1), (300, "f32", 1),
+                                         (40, "bf16", 1), (8, "f32", 2), (300, "f32", 2)])
+def test_shared_expert_adds_to_the_routed_output(torch, T, act, sfmt):
+    """The layer's routed output plus the shared expert (every token through one Q8_0 or 2-bit
+    expert) against the oracle's routed output plus its per-token shared expert.  The one expert
+    takes all T slots: 1 token runs on one-slot tiles, 8 and 32 on tiles of several slots, 40 and
+    300 (moe_large_tile_min: 33 and 12) on large tiles."""
     H, E, I, k, Is = 256, 8, 128, 2, 160
-    _say(f"shared expert {act}: T={T} H={H} I_shared={Is}")
+    _say(f"shared expert {act} fmt {sfmt}: T={T} H={H} I_shared={Is}")
     wl = synth.make(synth.custom(T, H, E, I, k, gate_fmt=2, up_fmt=2, down_fmt=1, router_fmt=1, act=act,
                                  name=f"shared_{act}"))
-    sg, su, sd = synth.shared_expert(0, H, Is)
+    sg, su, sd = synth.shared_expert(0, H, Is, sfmt)
     from quantized_moe_routed_amd.layer import SharedExpert
-    shared = SharedExpert(H, Is, 1, sg, su, sd)
+    shared = SharedExpert(H, Is, sfmt, sg, su, sd)
     layer = make_layer(wl)
     from quantized_moe_routed_amd.layer import act_code
     x = x_tensor(wl, torch)
@@ -543,5 +526,5 @@ def test_shared_expert_adds_to_the_routed_output(torch, T, act):
     layer.run(x, b)
     shared.add_to(x, b.out)
     torch.cuda.synchronize()
-    ref = oracle_expect(wl)["out"].astype(np.float64) + oracle.shared_expert((1, 1, 1), sg, su, sd, wl.x)
+    ref = oracle_expect(wl)["out"].astype(np.float64) + oracle.shared_expert((sfmt,) * 3, sg, su, sd, wl.x)
     assert_close(b.out.cpu().numpy(), ref, f"shared {act} T={T} out")

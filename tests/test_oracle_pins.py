@@ -248,6 +248,34 @@ def test_expert_closed_form_constant_rows():
     assert np.allclose(y, want, rtol=1e-12)
 
 
+def test_shared_expert_closed_form_per_token():
+    """oracle.shared_expert on a one-expert stack with constant rows (Q8_0 gate/up/down, and 2-bit
+    ones, value d q + m with every code equal): row t is c I SiLU(a S_t) (b S_t) in every column,
+    S_t the sum of token t's activations, for tokens of very different sizes."""
+    H, I, T = 64, 96, 5
+
+    def q8(rows, cols, q):
+        return np.frombuffer(b"".join(q8_block(2.0 ** -7, [q] * 32) for _ in range(rows * cols // 32)),
+                             np.uint8).reshape(1, rows, -1)
+
+    def q2(rows, cols, d, m, q):
+        return np.frombuffer(b"".join(q2_block(d, m, [q] * 32) for _ in range(rows * cols // 32)),
+                             np.uint8).reshape(1, rows, -1)
+
+    x = (synth.normal(4, 3, T * H).reshape(T, H) * np.array([1e-3, 0.1, 1.0, 10.0, 300.0])[:, None]).astype(np.float32)
+    S = x.astype(np.float64).sum(1)
+    cases = [((1, 1, 1), q8(I, H, 5), q8(I, H, -3), q8(H, I, 7), (5 / 128, -3 / 128, 7 / 128)),
+             ((2, 2, 2), q2(I, H, 2.0 ** -6, -2.0 ** -5, 3), q2(I, H, 2.0 ** -5, -2.0 ** -4, 1),
+              q2(H, I, 2.0 ** -6, 2.0 ** -6, 2), (1 / 64, -1 / 32, 3 / 64))]
+    for fm, g, u, d, (a, b, c) in cases:
+        rows = oracle.shared_expert(fm, g, u, d, x)
+        assert rows.shape == (T, H)
+        for t in range(T):
+            gt, ut = a * S[t], b * S[t]
+            want = c * I * (gt / (1 + math.exp(-gt))) * ut
+            assert np.allclose(rows[t], want, rtol=1e-12, atol=0.0), (fm, t)
+
+
 # ----------------------------------------------------------------- whole layer
 @pytest.mark.parametrize("case", ["cfg1", "q2sm_bias"])
 def test_layer_matches_brute_force(case):
