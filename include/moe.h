@@ -242,6 +242,24 @@ moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, in
                              int32_t* counts, int32_t* offsets, int32_t* slot_list, float* y_slot,
                              float* out, void* ws, size_t ws_bytes, hipStream_t s);
 
+/* The whole layer as moe_layer_forward, with the same arguments and results
+ * bit for bit, but without a workspace argument: for callers that cannot
+ * allocate device memory (code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid allocation).  The workspace is a 32 MiB array
+ * the library holds on each device from the moment it is loaded there until
+ * the process ends; this call allocates nothing.  Every call on a device uses
+ * that device's one array, so calls that overlap on one device (on different
+ * streams, or from different threads) race; the array keeps the last call's
+ * contents, none of which a later call reads before writing it.  A batch whose
+ * workspace (moe_workspace_size: route_ws + forward_ws) exceeds 32 MiB is
+ * refused with MOE_ERR_UNSUPPORTED (at H = 4096, I = 2048, E = 256, k = 8: up
+ * to 128 tokens fit).  Errors as for moe_layer_forward. */
+moe_status moe_layer_forward_noalloc(const void* x, int32_t xt, int32_t T, int32_t H, int32_t I, int32_t k,
+                                     const moe_qmat* router, const float* bias, const moe_experts* local,
+                                     const int32_t* g2l, int32_t E, int32_t E_local, int32_t* ids, float* w,
+                                     int32_t* counts, int32_t* offsets, int32_t* slot_list, float* y_slot,
+                                     float* out, hipStream_t s);
+
 /* ---- profiling ------------------------------------------------------------ */
 
 /* Record HIP events around launches of one kernel, for live per-kernel timing.

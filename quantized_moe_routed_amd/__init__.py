@@ -64,6 +64,8 @@ def _load():
     L.moe_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]
     L.moe_layer_forward.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(QMat), vp, ctypes.POINTER(Experts), vp,
                                     i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_layer_forward_noalloc.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(QMat), vp,
+                                            ctypes.POINTER(Experts), vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_planar_bytes.argtypes = [i32, i32, i32, psz, psz]
     L.moe_pack_planar.argtypes = [i32, i32, i32, i32, vp, vp, vp]
     L.moe_place_lpt.argtypes = [vp, i32, i32, vp]
@@ -72,7 +74,7 @@ def _load():
     L.moe_trace_kernel.argtypes = [ctypes.c_char_p, vp, vp, i32, ctypes.POINTER(ctypes.c_int32)]
     L.moe_trace_kernel_every.argtypes = [ctypes.c_char_p, vp, vp, i32, i32, ctypes.POINTER(ctypes.c_int32)]
     for f in ("moe_trace_kernel", "moe_trace_kernel_every", "moe_workspace_size", "moe_route", "moe_group_tokens", "moe_expert_forward", "moe_combine",
-              "moe_layer_forward", "moe_route_table", "moe_table_check",
+              "moe_layer_forward", "moe_layer_forward_noalloc", "moe_route_table", "moe_table_check",
               "moe_shared_expert_workspace", "moe_shared_expert_forward",
               "moe_planar_bytes", "moe_pack_planar", "moe_place_lpt", "moe_share_tables", "moe_plan_check"):
         getattr(L, f).restype = ctypes.c_int
@@ -84,7 +86,7 @@ lib = _load()
 EXPORTS = ("moe_last_error", "moe_version", "moe_large_tile_min", "moe_workspace_size", "moe_route", "moe_group_tokens",
            "moe_expert_forward", "moe_combine", "moe_layer_forward", "moe_planar_bytes", "moe_pack_planar", "moe_place_lpt",
            "moe_share_tables", "moe_plan_check", "moe_trace_kernel", "moe_trace_kernel_every", "moe_route_table",
-           "moe_table_check", "moe_shared_expert_workspace", "moe_shared_expert_forward")
+           "moe_table_check", "moe_shared_expert_workspace", "moe_shared_expert_forward", "moe_layer_forward_noalloc")
 
 
 def last_error() -> str:
@@ -160,6 +162,14 @@ def layer_forward(x, xt, T, H, I, k, router: QMat, bias, local: Experts, g2l, E,
     _check(lib.moe_layer_forward(_ptr(x), xt, T, H, I, k, ctypes.byref(router), _ptr(bias), ctypes.byref(local),
                                  _ptr(g2l), E, E_local, _ptr(ids), _ptr(w), _ptr(counts), _ptr(offsets),
                                  _ptr(slot_list), _ptr(y_slot), _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def layer_forward_noalloc(x, xt, T, H, I, k, router: QMat, bias, local: Experts, g2l, E, E_local, ids, w, counts,
+                          offsets, slot_list, y_slot, out, stream=None):
+    """moe_layer_forward on the library's own per-device scratch array: no workspace argument."""
+    _check(lib.moe_layer_forward_noalloc(_ptr(x), xt, T, H, I, k, ctypes.byref(router), _ptr(bias),
+                                         ctypes.byref(local), _ptr(g2l), E, E_local, _ptr(ids), _ptr(w), _ptr(counts),
+                                         _ptr(offsets), _ptr(slot_list), _ptr(y_slot), _ptr(out), _stream(stream)))
 
 
 # ---------------------------------------------------------------- host helpers

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdarg>
+#include <mutex>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -17,6 +18,9 @@
 namespace {
 
 thread_local std::string g_err;
+// set while a call runs on the library's own scratch array (its address is the library's, so the
+// caller-pointer check on the workspace is skipped)
+thread_local bool g_ws_is_scratch = false;
 
 moe_status fail(moe_status st, const char* fmt, ...) {
   char buf[512];
@@ -310,7 +314,7 @@ moe_status route_check(const char* fn, const void* x, int32_t xt, int32_t T, int
   dc(bias, "bias");
   dc(ids, "ids");
   dc(w, "w");
-  dc(ws, "workspace");
+  if (!g_ws_is_scratch) dc(ws, "workspace");
   return dc.st;
 }
 
@@ -390,7 +394,7 @@ moe_status forward_setup(const char* fn, const void* x, int32_t xt, int32_t T, i
   dc(offsets, "offsets");
   dc(slot_list, "slot_list");
   dc(y_slot, "y_slot");
-  dc(ws, "workspace");
+  if (!g_ws_is_scratch) dc(ws, "workspace");
   if (dc.st) return dc.st;
 
   char* wsb = reinterpret_cast<char*>(ws);
@@ -662,6 +666,67 @@ moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, in
   if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: FFN launch");
   e = moe::launch_combine(y_slot, w, ids, g2l, T, k, H, E, out, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer_forward: combine launch");
+  return ok();
+}
+
+// ---- the layer call without allocation: a workspace the library holds ---------------------
+// One array per device, of kScratchBytes, reserved when the library is loaded onto the device and
+// held until the process ends; its device address comes from hipGetSymbolAddress, once per
+// device with that device current, and every call on the device shares it.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of device dev's scratch array (looked up on the first call for the device).
+moe_status scratch_of(int dev, void** p) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_DEVICE, "device %d: no scratch slot", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "scratch: current device");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "scratch: set device");
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_fail(e, "scratch: hipGetSymbolAddress");
+    if (e2 != hipSuccess) return hip_fail(e2, "scratch: restore device");
+    if (!ptr) return fail(MOE_ERR_HIP, "scratch: no device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *p = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" moe_status moe_layer_forward_noalloc(const void* x, int32_t xt, int32_t T, int32_t H, int32_t I,
+                                                int32_t k, const moe_qmat* router, const float* bias,
+                                                const moe_experts* local, const int32_t* g2l, int32_t E,
+                                                int32_t E_local, int32_t* ids, float* w, int32_t* counts,
+                                                int32_t* offsets, int32_t* slot_list, float* y_slot, float* out,
+                                                hipStream_t s) {
+  const char* fn = "moe_layer_forward_noalloc";
+  if (T < 0 || H <= 0 || I <= 0 || k <= 0 || E <= 0 || E_local < 0 || E_local > E || E > kMaxE)
+    return fail(MOE_ERR_ARG, "%s: bad sizes", fn);
+  if (xt != MOE_ACT_F32 && xt != MOE_ACT_BF16) return fail(MOE_ERR_ARG, "%s: unknown activation type %d", fn, xt);
+  const size_t need = route_ws_bytes(T, E, H) + fwd_layout(T, H, I, k, E_local, xt).total;
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: this batch needs %zu bytes of workspace; the library's scratch holds %zu "
+                "(use moe_layer_forward with a caller workspace)", fn, need, kScratchBytes);
+  int dev = 0;
+  moe_status st = stream_device(s, &dev);
+  if (st) return st;
+  void* ws = nullptr;
+  if ((st = scratch_of(dev, &ws))) return st;
+  g_ws_is_scratch = true;
+  st = moe_layer_forward(x, xt, T, H, I, k, router, bias, local, g2l, E, E_local, ids, w, counts, offsets,
+                         slot_list, y_slot, out, ws, kScratchBytes, s);
+  g_ws_is_scratch = false;
+  if (st) return st;
   return ok();
 }
 

@@ -14,7 +14,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (ACT_BF16, ACT_F32, W_F32, Experts, combine, expert_forward, group_tokens, layer_forward, pack_planar,
+from . import (ACT_BF16, ACT_F32, W_F32, Experts, combine, expert_forward, group_tokens, layer_forward,
+               layer_forward_noalloc, pack_planar,
                plan_check,
                qmat, route, route_table, shared_expert_forward, shared_expert_workspace, table_check,
                workspace_size)
@@ -145,6 +146,15 @@ class MoELayer:
         layer_forward(x, b.xt, b.T, self.H, self.I, self.k, self._router_q, self.bias, self._experts, self.g2l,
                       self.E, self.E_local, b.ids, b.w, b.counts, b.offsets, b.slot_list, b.y_slot, b.out, b.ws,
                       b.ws.numel(), stream)
+        return b.out
+
+
+    def run_noalloc(self, x: torch.Tensor, b: Buffers, stream=None):
+        """The layer as one call on the library's own scratch (moe_layer_forward_noalloc): b's
+        workspace is not used; results equal run's bit for bit."""
+        layer_forward_noalloc(x, b.xt, b.T, self.H, self.I, self.k, self._router_q, self.bias, self._experts,
+                              self.g2l, self.E, self.E_local, b.ids, b.w, b.counts, b.offsets, b.slot_list, b.y_slot,
+                              b.out, stream)
         return b.out
 
 
