@@ -134,7 +134,10 @@ moe_status moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t k, int32_
  * work; the choice changes speed only, never results. */
 int32_t moe_large_tile_min(int32_t T);
 
-/* Router scoring and top-k selection (one token per row of x).
+/* Router scoring and top-k selection (one token per row of x): the routing
+ * step of the layer above, which the pages assume rather than write out (the
+ * expert-parallel page, "Stage 1 -- EP=2", partitions exactly these routed
+ * slots).
  *   x      : [T, H] fp32 or bf16 (xt), row-major.
  *   router : rows = E, cols = H, n = 1; format F32 or Q8_0.
  *   bias   : [E] fp32 added to every logit (used for selection and weights), or NULL.
@@ -185,7 +188,10 @@ moe_status moe_shared_expert_forward(const void* x, int32_t xt, int32_t T, int32
  * no expert twice in a row.  MOE_ERR_ARG names the first offending entry. */
 moe_status moe_table_check(const int32_t* table, int32_t V, int32_t k, int32_t E);
 
-/* Group the T*k routing slots (slot s = t*k + j) by expert.
+/* Group the T*k routing slots (slot s = t*k + j) by expert: per-expert token
+ * lists and loads, the quantities the expert-parallel page weighs ("Stage 0":
+ * tokens are compute, distinct experts are bytes; the load counter is a device
+ * array read outside captured work).
  *   counts    : [E] int32 out, slots routed to each expert (the per-expert token
  *               load; the number of non-zero entries is the count of distinct
  *               experts the batch touches).
@@ -209,10 +215,13 @@ moe_status moe_group_tokens(const int32_t* ids, int32_t T, int32_t k, int32_t E,
  * E_local must equal local->n_experts; the table's consistency is checked once
  * on the host with moe_plan_check().  Every product runs on the fp16 matrix
  * cores: weight codes enter them as exact small integers, block scales are
- * applied in fp32 per 32-block, the activations enter as an fp16 hi + lo pair
- * (fp32 x, 22 significant bits) or one fp16 plane (bf16 x), each token scaled
- * by a power of two, and the intermediate silu(g)*u enters the down projection
- * as an fp16 hi + lo pair (it must stay below 65504 in magnitude).  No path
+ * applied in fp32 per 32-block.  The activations enter as an fp16 hi + lo
+ * pair (fp32 x) or one fp16 plane (bf16 x), and the intermediate silu(g)*u
+ * as an fp16 hi + lo pair, each row of either scaled by the power of two that
+ * brings its largest magnitude to [2^14, 2^15) (single-token batches: each
+ * 32-value block of silu(g)*u by its own): a value within 2^18 of its row's
+ * (block's) largest keeps 22 significant bits, smaller ones an absolute error
+ * below 2^-39 of that largest, and any finite input is in range.  No path
  * uses floating-point atomics; results do not depend on scheduling.
  * Limits: H and I multiples of 32, H <= 8192, I <= 8192. */
 moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, int32_t I, int32_t k,
@@ -220,7 +229,10 @@ moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, i
                               const int32_t* counts, const int32_t* offsets, const int32_t* slot_list,
                               float* y_slot, void* ws, size_t ws_bytes, hipStream_t s);
 
-/* Weighted combine: out[t] = sum over j = 0..k-1 in that order, of owned slots,
+/* Weighted combine (the expert-parallel page, "Stage 1 -- EP=2": a share's
+ * partial is the sum over the slots it owns; TrevorS/ds4 PR #13, "Tested": no
+ * float atomics, so runs are bit-identical):
+ * out[t] = sum over j = 0..k-1 in that order, of owned slots,
  * of w[t,j] * y_slot[t*k+j], starting from +0.0, in fp32, with no atomics.
  * g2l NULL = every slot owned.  out: [T, H] fp32. */
 moe_status moe_combine(const float* y_slot, const float* w, const int32_t* ids, const int32_t* g2l,

@@ -37,7 +37,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MOE_ORACLE_LIB names another build of the same source (the sanitizer test builds one with
+# -fsanitize=address,undefined); it is loaded as it is, without building
+_LIB_OVERRIDE = os.environ.get("MOE_ORACLE_LIB")
+_LIB_PATH = _LIB_OVERRIDE or os.path.join(_HERE, "liboracle.so")
 _lib = None
 _lock = threading.Lock()
 
@@ -46,6 +49,8 @@ _BLOCK = {Q8_0: 34, Q2SM: 12}
 
 
 def build(force: bool = False) -> str:
+    if _LIB_OVERRIDE:
+        return _LIB_PATH
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
@@ -108,7 +113,7 @@ def route(x: np.ndarray, router_fmt: int, router: np.ndarray, bias: Optional[np.
     T, H = x.shape
     router = np.ascontiguousarray(router, dtype=np.uint8).reshape(-1, row_bytes(router_fmt, H))
     E = router.shape[0]
-    assert 1 <= k <= min(E, 64)
+    assert 1 <= k <= E
     b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
     ids = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float32)

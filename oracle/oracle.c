@@ -147,7 +147,8 @@ void oracle_route(const float* x, int T, int H, int E, int router_fmt, const uin
     for (int e = 0; e < E; ++e)
       z[e] = oracle_router_logit(router_fmt, router + rb * e, x + (int64_t)t * H, H, bias ? bias + e : NULL);
     if (z_out) memcpy(z_out + (int64_t)t * E, z, sizeof(float) * (size_t)E);
-    double s[64], ssum = 0.0;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+    double ssum = 0.0;
     for (int j = 0; j < k; ++j) {
       int best = -1;
       for (int e = 0; e < E; ++e) {
@@ -160,6 +161,7 @@ void oracle_route(const float* x, int T, int H, int E, int router_fmt, const uin
     }
     for (int j = 0; j < k; ++j) ssum += s[j];
     for (int j = 0; j < k; ++j) w[(int64_t)t * k + j] = (float)(s[j] / ssum);
+    free(s);
     free(z);
     free(taken);
   }

@@ -26,6 +26,7 @@ SOURCES = {
     "ffn_large.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "combine.hip": [],
     "api.cpp": [],
+    "host.cpp": [],
 }
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

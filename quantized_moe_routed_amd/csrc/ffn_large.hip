@@ -510,14 +510,12 @@ __global__ __launch_bounds__((LargeCfg<F, NM, LO, MODE, NT2, WM, CG>::THREADS), 
 template <int F, int NM, bool LO, int MODE, int NT2, int WM, int CG>
 static hipError_t launch_large_t(const FfnTileArgs& t, int max_tiles, hipStream_t s) {
   using C = LargeCfg<F, NM, LO, MODE, NT2, WM, CG>;
-  static bool attr_set = false;
   const size_t lds = 2 * (size_t)C::STAGE;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_large_kernel<F, NM, LO, MODE, NT2, WM, CG>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // set on every launch (a host-side call): the attribute belongs to the kernel on the device that
+  // launches it, and no state is kept between calls
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_large_kernel<F, NM, LO, MODE, NT2, WM, CG>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   const int n_ct = (t.N + C::BN - 1) / C::BN;
   const int grid = 8 * n_ct * ((max_tiles + 7) / 8);
   return launch_stamped(ffn_large_kernel<F, NM, LO, MODE, NT2, WM, CG>, dim3(grid), dim3(C::THREADS), lds, s, t, n_ct);

@@ -37,7 +37,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gen.c")
-_LIB_PATH = os.path.join(_HERE, "libsynth.so")
+# MOE_SYNTH_LIB names another build of the same source (the sanitizer test builds one with
+# -fsanitize=address,undefined); it is loaded as it is, without building
+_LIB_OVERRIDE = os.environ.get("MOE_SYNTH_LIB")
+_LIB_PATH = _LIB_OVERRIDE or os.path.join(_HERE, "libsynth.so")
 _lib = None
 _lock = threading.Lock()
 
@@ -53,6 +56,8 @@ W_SIGMA = 0.02
 
 
 def build(force: bool = False) -> str:
+    if _LIB_OVERRIDE:
+        return _LIB_PATH
     """Compile gen.c into libsynth.so (gcc, OpenMP)."""
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()

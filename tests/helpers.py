@@ -57,3 +57,39 @@ def oracle_expect(wl, tokens=None, l2g=None, g2l=None):
         gate, up, down = wl.gate[l2g], wl.up[l2g], wl.down[l2g]
     return oracle.layer(wl.x, wl.cfg.router_fmt, wl.router[0], wl.bias, wl.k, fmts(wl), gate, up, down,
                         g2l=g2l, tokens=tokens)
+
+
+def decode_planar(fmt, codes, scales, n, rows, cols):
+    """Values of n planar matrices, decoded from the row-group layout as include/moe.h documents it."""
+    nb = cols // 32
+    if fmt == 0:
+        return codes.view(np.float32).astype(np.float64).reshape(n * rows, cols)
+    rg = (rows + 15) // 16
+    out = np.zeros((n, rg * 16, cols))
+    if fmt == 1:
+        nu = (nb + 1) // 2
+        c = codes.reshape(n, rg, nu, 16, 64)
+        d = scales.view(np.float16).astype(np.float64).reshape(n, rg, nu, 16, 2)
+        for b in range(nb):
+            u, h = b // 2, b % 2
+            for g in range(4):
+                q = c[:, :, u, :, 16 * g + 8 * h:16 * g + 8 * h + 8].view(np.int8).astype(np.float64)
+                out[:, :, 32 * b + 8 * g:32 * b + 8 * g + 8] = (d[:, :, u, :, h:h + 1] * q).reshape(n, rg * 16, 8)
+    else:
+        nu = (nb + 7) // 8
+        c = codes.reshape(n, rg, nu, 16, 64)
+        sc = scales.view(np.float16).astype(np.float64).reshape(n, rg, nu, 2, 16, 8)   # d rows, then m rows
+        for b in range(nb):
+            u, k = b // 8, b % 8
+            i, h = k // 2, k % 2
+            d = sc[:, :, u, 0, :, k].reshape(n, rg * 16)
+            m = sc[:, :, u, 1, :, k].reshape(n, rg * 16)
+            for g in range(4):
+                lo_byte = c[:, :, u, :, 16 * g + 4 * i + h].reshape(n, rg * 16)       # definition byte 2g
+                hi_byte = c[:, :, u, :, 16 * g + 4 * i + 2 + h].reshape(n, rg * 16)   # definition byte 2g+1
+                for s in range(4):
+                    out[:, :, 32 * b + 8 * g + s] = d * ((lo_byte >> (2 * s)) & 3) + m
+                    out[:, :, 32 * b + 8 * g + 4 + s] = d * ((hi_byte >> (2 * s)) & 3) + m
+    # rows that pad the last group hold zeros
+    assert not out[:, rows:, :].any()
+    return out[:, :rows, :].reshape(n * rows, cols)
