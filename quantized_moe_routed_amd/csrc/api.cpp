@@ -124,7 +124,9 @@ TilePlan tile_plan(int T, int H, int I, int k, int E_local, int xt) {
   const bool large = lmin > 0;
   p.large_min = large ? lmin : 0x7FFFFFFF;
   p.bm_small = moe::small_tile_rows(H, I, xt == MOE_ACT_F32);
-  p.max_small = (int)max_tiles(slots, std::min<int64_t>(E_local, slots), p.bm_small);
+  // (one token: each of its k experts is a tile of one slot, so at most min(k, E_local) tiles; the
+  // launches' grids hold exactly the tiles that can occur)
+  p.max_small = T == 1 ? std::min(k, E_local) : (int)max_tiles(slots, std::min<int64_t>(E_local, slots), p.bm_small);
   p.max_large = large ? (int)max_tiles(slots, std::min<int64_t>(E_local, slots / lmin), kLargeTile) : 0;
   return p;
 }

@@ -49,8 +49,10 @@ constexpr int kStageRows = kSmallRowsMax;   // slots per tile at most; their act
 // ONE: every tile holds a single slot (one token in the batch), so only the
 // first component of each output fragment is ever needed.
 // SEL (gate/up of batches of at most kSelMaxTokens tokens): the workgroup first selects, groups
-// and numbers the tiles itself from the logits (smallsel.h); one workgroup of an extra grid row
-// stores the routing results and the tile list for the later launches.
+// and numbers the tiles itself from the logits (smallsel.h); workgroup (0, 0) also stores the
+// routing results and the tile list for the later launches.  (As a workgroup of its own, in a grid
+// row past the tiles, it would be dispatched only once a tile's workgroup had finished, and its
+// selection would then end the launch several microseconds after the last tile.)
 // Bytes of the activation staging area (rows hi [+ lo], then a row of zeros), rounded to 16: the
 // one-token selection keeps its candidates past it, and the one-slot reduction its sums past those.
 __host__ __device__ constexpr size_t sel_cand_offset(int stage_rows, int K, bool lo) {
@@ -59,6 +61,7 @@ __host__ __device__ constexpr size_t sel_cand_offset(int stage_rows, int K, bool
 __host__ __device__ constexpr size_t one_red_offset(bool sel, int stage_rows, int K, bool lo) {
   return sel_cand_offset(stage_rows, K, lo) + (sel ? kSelScratchBytes : 0);
 }
+
 
 
 template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL>
@@ -73,9 +76,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   const int tile = blockIdx.y;
   int4 tl, tk0, tk1;   // the tile; the operand rows of its slots 0..3 and 4..7
   if constexpr (SEL) {
-    // the grid's last row holds no tile: its workgroup 0 stores the routing results
-    const bool writer = blockIdx.y == gridDim.y - 1;
-    if (writer && blockIdx.x != 0) return;
+    const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
     if constexpr (ONE) {
       // each wave selects by itself; its candidates sit past the staging area, which faster waves
       // start to fill while slower ones still select
@@ -83,12 +84,12 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
       uint64_t* cand = reinterpret_cast<uint64_t*>(smem + sel_cand_offset(a.stage_rows, a.K, LO)) +
                        (size_t)(threadIdx.x / kWave) * (a.sel.E + kThrMaxK);
       tl = tk0 = tk1 = make_int4(0, 0, 0, 0);
-      const int n = one_token_select(a.sel, writer, writer ? -1 : tile, cand, tl);
-      if (writer || tile >= n) return;
+      const int n = one_token_select(a.sel, writer, tile, cand, tl);
+      if (tile >= n) return;
     } else {
       __shared__ SelLds sl;
-      small_select<kFfnThreads>(a.sel, sl, writer, writer ? -1 : tile, reinterpret_cast<uint64_t*>(smem));
-      if (writer || tile >= sl.n_tiles) return;
+      small_select<kFfnThreads>(a.sel, sl, writer, tile, reinterpret_cast<uint64_t*>(smem));
+      if (tile >= sl.n_tiles) return;
       tl = sl.tile;
       tk0 = sl.tok[0];
       tk1 = sl.tok[1];
@@ -598,7 +599,7 @@ static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  return launch_stamped(kern, dim3(t.N / (16 * kNT), max_tiles + (SEL ? 1 : 0)), dim3(kFfnThreads), lds, s, t);
+  return launch_stamped(kern, dim3(t.N / (16 * kNT), max_tiles), dim3(kFfnThreads), lds, s, t);
 }
 
 int small_tile_rows(int H, int I, bool f32_act) {
