@@ -78,14 +78,23 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   if constexpr (SEL) {
     const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
     if constexpr (ONE) {
-      // each wave selects by itself; its candidates sit past the staging area, which faster waves
-      // start to fill while slower ones still select
-      static_assert(kFfnWaves <= kSelMaxTokens, "one candidate area per wave");
-      uint64_t* cand = reinterpret_cast<uint64_t*>(smem + sel_cand_offset(a.stage_rows, a.K, LO)) +
-                       (size_t)(threadIdx.x / kWave) * (a.sel.E + kThrMaxK);
+      // wave 0 selects (its candidates sit past the staging area) and hands the tile to the other
+      // waves through LDS: a selection in every wave would put four copies of the same work on
+      // each SIMD
+      __shared__ int4 s_tl;
+      __shared__ int s_n;
       tl = tk0 = tk1 = make_int4(0, 0, 0, 0);
-      const int n = one_token_select(a.sel, writer, tile, cand, tl);
-      if (tile >= n) return;
+      if (threadIdx.x < kWave) {
+        uint64_t* cand = reinterpret_cast<uint64_t*>(smem + sel_cand_offset(a.stage_rows, a.K, LO));
+        const int n = one_token_select(a.sel, writer, tile, cand, tl);
+        if (threadIdx.x == 0) {
+          s_tl = tl;
+          s_n = n;
+        }
+      }
+      __syncthreads();
+      if (tile >= s_n) return;
+      tl = s_tl;
     } else {
       __shared__ SelLds sl;
       small_select<kFfnThreads>(a.sel, sl, writer, tile, reinterpret_cast<uint64_t*>(smem));

@@ -132,12 +132,12 @@ __device__ __forceinline__ void small_select(const SelArgs& a, SelLds& L, bool w
 }
 
 // One token: its k experts are distinct, so every selected expert holds one slot and, when owned,
-// one tile, and the stable counting sort reduces to ranks.  Each wave selects by itself (cand: its
-// own E + kThrMaxK entries of LDS) and finds its workgroup's tile with no LDS exchange and no
-// barrier: slot j's position is the number of selected ids below id_j, its tile number the number
-// of owned selected ids below id_j (tiles in ascending expert id, as in small_select).  Wave 0 of
-// the writer stores what small_select stores for one token.  Returns the tile count; tl receives
-// tile want when want is below it (its one row is token 0).
+// one tile, and the stable counting sort reduces to ranks.  One wave selects (cand: E + kThrMaxK
+// entries of LDS) and finds tile want with no LDS exchange: slot j's position is the number of
+// selected ids below id_j, its tile number the number of owned selected ids below id_j (tiles in
+// ascending expert id, as in small_select).  Wave 0 of the writer stores what small_select stores
+// for one token.  Returns the tile count; tl receives tile want when want is below it (its one row
+// is token 0).
 __device__ __forceinline__ int one_token_select(const SelArgs& a, bool writer, int want, uint64_t* cand,
                                                 int4& tl) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
