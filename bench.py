@@ -15,7 +15,13 @@ parallel share) measured the same way, under "workloads".
 
 Kernel times come from HIP events that the library records around every
 eighth launch of the named kernel during the timed region (on the stream the
-kernel runs on).
+kernel runs on).  The timed region is also cut into ten chunks, whose per-step
+times give p10 / median / p90.  For the decode-like workloads two more numbers
+are taken, each labelled: cold (a 512 MB buffer written between steps, outside
+the timed steps, so nothing of the step's weights survives in the 256 MB last-
+level cache) and warm (the same batch every step, its experts' weights served
+from that cache).  Fractions are given against the published peaks and against
+a measured device copy.
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -82,6 +88,7 @@ def input_pool(wl, n_batches, torch):
 
 
 TRACE_EVERY = 8  # the kernel events of the timed region sample one launch in this many
+N_CHUNKS = 10    # the timed region in this many chunks, for percentiles of the step time
 
 
 def time_layer(layer, xs, steps, warmup, kernel, torch, run=None, route=None):
@@ -100,16 +107,19 @@ def time_layer(layer, xs, steps, warmup, kernel, torch, run=None, route=None):
     # events around every TRACE_EVERY-th launch of the kernel only: each pair of events costs the
     # stream a few microseconds, which would otherwise be charged to every step
     trace = moe.KernelTrace(kernel, (steps + TRACE_EVERY - 1) // TRACE_EVERY, TRACE_EVERY)
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    n_chunks = min(N_CHUNKS, steps)
+    bounds = [round(steps * c / n_chunks) for c in range(n_chunks + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in bounds]
     torch.cuda.synchronize()
     with trace:
-        start.record()
-        for i in range(steps):
-            run((warmup + i) % len(xs), b)
-        end.record()
+        evs[0].record()
+        for c in range(n_chunks):
+            for i in range(bounds[c], bounds[c + 1]):
+                run((warmup + i) % len(xs), b)
+            evs[c + 1].record()
     torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / steps
+    ms_step = evs[0].elapsed_time(evs[-1]) / steps
+    chunk_ms = [evs[c].elapsed_time(evs[c + 1]) / (bounds[c + 1] - bounds[c]) for c in range(n_chunks)]
     kms = trace.times_ms()
     # per-step loads, outside the timed region: replay the routing of each batch and count the
     # owned experts and slots on each kind of tile
@@ -129,8 +139,56 @@ def time_layer(layer, xs, steps, warmup, kernel, torch, run=None, route=None):
         d_large.append(int((c >= large_min).sum()))
         s_large.append(int(c[c >= large_min].sum()))
     torch.cuda.synchronize()
+    pct = {f"ms_{q}": float(np.percentile(chunk_ms, v)) for q, v in (("p10", 10), ("median", 50), ("p90", 90))}
     return (ms_step, float(np.mean(kms)), float(np.mean(d_small)), float(np.mean(s_small)), float(np.mean(d_large)),
-            float(np.mean(s_large)))
+            float(np.mean(s_large)), pct)
+
+
+FLUSH_BYTES = 512 << 20   # written between cold steps: twice the last-level cache
+
+
+def time_cold_warm(layer, xs, reps, torch, run=None):
+    """Per-step times (median ms) of single steps: cold, with FLUSH_BYTES written to a scratch
+    buffer before each step (outside its events), and warm, the same batch repeated."""
+    from quantized_moe_routed_amd.layer import act_code
+    b = layer.buffers(xs[0].shape[0], act_code(xs[0]))
+    run = run or (lambda i, b: layer.run(xs[i], b))
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for r in range(reps):
+        flush.fill_(r & 0xFF)
+        evs[r][0].record()
+        run(r % len(xs), b)
+        evs[r][1].record()
+    torch.cuda.synchronize()
+    cold = float(np.median([s.elapsed_time(e) for s, e in evs]))
+    for _ in range(5):
+        run(0, b)
+    for r in range(reps):
+        evs[r][0].record()
+        run(0, b)
+        evs[r][1].record()
+    torch.cuda.synchronize()
+    warm = float(np.median([s.elapsed_time(e) for s, e in evs]))
+    del flush
+    return cold, warm
+
+
+def copy_ceiling_gbs(torch, nbytes=1 << 30, reps=10):
+    """Measured device copy rate (bytes read + written per second, GB/s) over nbytes."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (s.elapsed_time(e) * 1e-3) / 1e9
+    del src, dst
+    return gbs
 
 
 def traffic_record(kernel):
@@ -151,7 +209,7 @@ def traffic_record(kernel):
     return rec if h.hexdigest() == rec["sources_sha256"] else None
 
 
-def measure(name, steps, warmup, torch):
+def measure(name, steps, warmup, torch, copy_gbs=None):
     cfg_id = WORKLOADS[name]
     share = 0 if name == "ep_share" else None
     log(f"{name}: generating weights and inputs")
@@ -180,7 +238,7 @@ def measure(name, steps, warmup, torch):
         run = lambda i, b: layer.run_table(xs[i], b, tids[i], table)
         route = lambda i, b: layer.route_table(xs[i], b, tids[i], table)
     log(f"{name}: timing {steps} steps")
-    ms, kms, d_small, s_small, d_large, s_large = time_layer(layer, xs, steps, warmup, kernel, torch, run, route)
+    ms, kms, d_small, s_small, d_large, s_large, pct = time_layer(layer, xs, steps, warmup, kernel, torch, run, route)
     slots = s_small + s_large
     router_bytes = layer.router.nbytes()
     x_bytes = T * H * (2 if bf16 else 4)
@@ -192,6 +250,7 @@ def measure(name, steps, warmup, torch):
     res = {
         "tokens_per_s": T / (ms * 1e-3),
         "ms_per_step": ms,
+        **pct,
         "T": T,
         "owned_slots": slots,
         "distinct_experts": d_small + d_large,
@@ -203,54 +262,109 @@ def measure(name, steps, warmup, torch):
         "layer_tflops": flops / (ms * 1e-3) / 1e12,
         "mfma_frac_of_bf16_peak": (flops / (ms * 1e-3) / 1e12) / BF16_PEAK_TFLOPS if bf16 else None,
     }
+    # the whole layer against its binding roofline (HBM, or the matrix cores for prefill)
+    if name == "prefill":
+        res["layer_roofline"] = {"bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                 "algorithmic_flops_per_step": flops}
+    else:
+        res["layer_roofline"] = {"bound": "hbm", "achieved": res["layer_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": res["layer_gbs"] / HBM_PEAK_GBS, "algorithmic_bytes_per_step": layer_bytes}
+        if copy_gbs:
+            res["layer_roofline"]["copy_ceiling_gbs"] = copy_gbs
+            res["layer_roofline"]["frac_of_copy_ceiling"] = res["layer_gbs"] / copy_gbs
+    if name in ("decode", "batched_decode", "ep_share"):
+        log(f"{name}: cold and warm single steps")
+        cold, warm = time_cold_warm(layer, xs, 30, torch, run)
+        res["cold"] = {"ms_per_step": cold, "layer_gbs": layer_bytes / (cold * 1e-3) / 1e9,
+                       "note": f"{FLUSH_BYTES >> 20} MB written before each step, outside its events"}
+        res["warm"] = {"ms_per_step": warm, "layer_gbs": layer_bytes / (warm * 1e-3) / 1e9,
+                       "note": "the same batch every step: its experts' weights come from the last-level cache"}
     if name == "prefill":
         # large-tile gate/up: 2 matrices x 2 flops x H x I per slot on large tiles
         kflops = 4.0 * H * I * s_large
+        rec = traffic_record(kernel + ":" + name)
         res["roofline"] = {"bound": "mfma", "achieved": kflops / (kms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": kflops / (kms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                           "traffic": None, "algorithmic_flops_per_launch": kflops}
+                           "traffic": rec["bytes_per_launch"] if rec else None, "algorithmic_flops_per_launch": kflops}
     else:
-        # small-tile gate/up: the gate/up weights of the experts on small tiles, per slot the
-        # fp16 activation operand read (hi + lo: 4 bytes a value) and h written (hi + lo)
-        kbytes = d_small * gateup_per_expert + s_small * (H * 4 + I * 4)
+        # small-tile gate/up, algorithmic bytes as for the layer: the gate/up weights of the experts
+        # on small tiles and the activations x; the implementation's own traffic (the prepared
+        # operand read per slot, hi + lo, and h written per slot, hi + lo) is reported beside it
+        kbytes = d_small * gateup_per_expert + x_bytes
+        impl = s_small * (H * 4 + I * 4)
         rec = traffic_record(kernel + ":" + name)
         res["roofline"] = {"bound": "hbm", "achieved": kbytes / (kms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": kbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                            "traffic": rec["bytes_per_launch"] if rec else None,
-                           "algorithmic_bytes_per_launch": kbytes}
+                           "algorithmic_bytes_per_launch": kbytes, "implementation_bytes_per_launch": impl}
     res["roofline"]["kernel"] = kernel
     res["roofline"]["avg_launch_ms"] = kms
     return wl, res
 
 
-def cpu_baseline(budget_s=15.0, max_tokens=1600):
-    """The CPU oracle, as it stands, on a bounded sample of the decode workload."""
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo where there is one)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(budget_s=15.0, single_budget_s=8.0, max_tokens=1600):
+    """The CPU oracle, as it stands, on a bounded sample of the decode workload: on every thread its
+    OpenMP runtime uses, then on one thread."""
+    import ctypes
     import oracle
     import synth
     wl = synth.make(2, T=1)
     fm = (wl.cfg.gate_fmt, wl.cfg.up_fmt, wl.cfg.down_fmt)
     pool = synth.tokens(0, max_tokens, wl.H)
-    done = 0
-    t0 = time.perf_counter()
-    while done < max_tokens and time.perf_counter() - t0 < budget_s:
-        xs = pool[done:done + 8]
-        oracle.layer(xs, wl.cfg.router_fmt, wl.router[0], wl.bias, wl.k, fm, wl.gate, wl.up, wl.down)
-        done += len(xs)
-    dt = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    def run(budget, limit):
+        done = 0
+        t0 = time.perf_counter()
+        while done < limit and time.perf_counter() - t0 < budget:
+            xs = pool[done:done + 8]
+            oracle.layer(xs, wl.cfg.router_fmt, wl.router[0], wl.bias, wl.k, fm, wl.gate, wl.up, wl.down)
+            done += len(xs)
+        return done, time.perf_counter() - t0
+
+    gomp = ctypes.CDLL("libgomp.so.1")   # the oracle's OpenMP runtime (already loaded with it)
+    threads = int(gomp.omp_get_max_threads())
+    done, dt = run(budget_s, max_tokens)
+    gomp.omp_set_num_threads(1)
+    try:
+        done1, dt1 = run(single_budget_s, max_tokens)
+    finally:
+        gomp.omp_set_num_threads(threads)
     return {"value": done / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
             "sample": f"{done} single-token decode layer evaluations (route + 8 experts + combine, fp64 FFN) "
-                      f"in {dt:.1f} s"}
+                      f"in {dt:.1f} s on {threads} OpenMP threads",
+            "single_thread": {"value": done1 / dt1, "unit": "tokens/s",
+                              "sample": f"{done1} evaluations in {dt1:.1f} s on one thread"}}
 
 
 # Kernels whose HBM traffic is recorded from hardware counters, by workload, with the sources that
 # define them (the record is ignored once any of them changes).
-TRAFFIC_KERNELS = {
-    "decode": ("ffn_gateup", "moe::ffn_small_kernel<2, 2, true, 0, true, true>",
-               ["quantized_moe_routed_amd/csrc/ffn.hip", "quantized_moe_routed_amd/csrc/ffn.h",
+_FFN_SOURCES = ["quantized_moe_routed_amd/csrc/ffn.hip", "quantized_moe_routed_amd/csrc/ffn.h",
                 "quantized_moe_routed_amd/csrc/fmt.h", "quantized_moe_routed_amd/csrc/device.h",
                 "quantized_moe_routed_amd/csrc/smallsel.h", "quantized_moe_routed_amd/csrc/select.h",
-                "quantized_moe_routed_amd/csrc/launch.h"]),
+                "quantized_moe_routed_amd/csrc/launch.h"]
+TRAFFIC_KERNELS = {
+    "decode": ("ffn_gateup", "moe::ffn_small_kernel<2, 2, true, 0, true, true>", _FFN_SOURCES),
+    "batched_decode": ("ffn_gateup", "moe::ffn_small_kernel<2, 2, true, 0, false, false>", _FFN_SOURCES),
+    "ep_share": ("ffn_gateup", "moe::ffn_small_kernel<2, 2, true, 0, false, false>", _FFN_SOURCES),
+    "prefill": ("ffn_gateup_large", "moe::ffn_large_kernel<2, 2, false, 0, 1, 2, 4>",
+                ["quantized_moe_routed_amd/csrc/ffn_large.hip", "quantized_moe_routed_amd/csrc/ffn.h",
+                 "quantized_moe_routed_amd/csrc/fmt.h", "quantized_moe_routed_amd/csrc/device.h",
+                 "quantized_moe_routed_amd/csrc/launch.h"]),
 }
 COPY_BYTES = 256 << 20   # the calibration copy: reads and writes this many bytes
 
@@ -333,7 +447,9 @@ def main():
 
     if args.calibration_copy:
         calibration_copy(torch)
-    wl, head = measure(args.workload, args.steps, args.warmup, torch)
+    copy_gbs = copy_ceiling_gbs(torch)
+    log(f"device copy: {copy_gbs:.0f} GB/s (read + write)")
+    wl, head = measure(args.workload, args.steps, args.warmup, torch, copy_gbs)
     others = {}
     if not args.only:
         for name in ("batched_decode", "prefill", "ep_share", "table_batched", "decode_shared", "decode"):
@@ -341,7 +457,7 @@ def main():
                 continue
             steps = {"prefill": 20, "batched_decode": 100, "ep_share": 50, "table_batched": 100, "decode_shared": 200,
                      "decode": 200}[name]
-            _, r = measure(name, steps, 5, torch)
+            _, r = measure(name, steps, 5, torch, copy_gbs)
             others[name] = r
     T = head["T"]
     cfg = wl.cfg
@@ -372,11 +488,19 @@ def main():
         "dtype": "bf16" if cfg.act == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": desc, "global_batch": T, "parallelism": "none (1 GPU)"},
+        "ms_p10": head["ms_p10"],
+        "ms_median": head["ms_median"],
+        "ms_p90": head["ms_p90"],
         "layer_gbs": head["layer_gbs"],
         "layer_bytes_per_step": head["layer_bytes"],
         "distinct_experts_per_step": head["distinct_experts"],
         "roofline": head["roofline"],
+        "layer_roofline": head["layer_roofline"],
+        "measured_copy_gbs": copy_gbs,
     }
+    for key in ("cold", "warm"):
+        if key in head:
+            result[key] = head[key]
     if head["mfma_frac_of_bf16_peak"] is not None:
         result["mfma_frac_of_bf16_peak"] = head["mfma_frac_of_bf16_peak"]
     if others:
