@@ -127,6 +127,12 @@ TilePlan tile_plan(int T, int H, int I, int k, int E_local, int xt) {
   // (one token: each of its k experts is a tile of one slot, so at most min(k, E_local) tiles; the
   // launches' grids hold exactly the tiles that can occur)
   p.max_small = T == 1 ? std::min(k, E_local) : (int)max_tiles(slots, std::min<int64_t>(E_local, slots), p.bm_small);
+  // with large tiles, small tiles take only experts of fewer than large_min slots: at most
+  // ceil((large_min - 1) / bm_small) tiles each (the launches' grids hold max_small tiles, and a
+  // workgroup past the tile count only reads the count and ends)
+  if (large)
+    p.max_small = (int)std::min<int64_t>(p.max_small, std::min<int64_t>(E_local, slots) *
+                                                          ((lmin - 1 + p.bm_small - 1) / p.bm_small));
   p.max_large = large ? (int)max_tiles(slots, std::min<int64_t>(E_local, slots / lmin), kLargeTile) : 0;
   return p;
 }

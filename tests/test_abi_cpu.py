@@ -190,8 +190,11 @@ def test_bf16_forward_format_limits():
     f = moe.workspace_size(2048, 4096, 2048, 8, 256, 256, moe.ACT_F32)
     assert a[2] >= 2048 * 8 * 2048 * 4 + 2048 * 4096 * 2
     # fp32 activations add the lo plane and, their staging of 8 rows not fitting two workgroups per
-    # compute unit at H = 4096, take small tiles of 4 slots: 2048 more tiles of 16 + 32 bytes
-    assert f[2] == a[2] + 2048 * 4096 * 2 + (16384 // 4 - 16384 // 8) * (16 + 32)
+    # compute unit at H = 4096, take small tiles of 4 slots.  Large tiles take every expert of 12
+    # slots or more (T = 2048), so an expert has at most ceil(11 / 4) = 3 small tiles of 4 slots
+    # against ceil(11 / 8) = 2 of 8: 256 more tiles of 16 + 32 bytes
+    assert moe.large_tile_min(2048) == 12
+    assert f[2] == a[2] + 2048 * 4096 * 2 + 256 * (3 - 2) * (16 + 32)
 
 
 def test_build_scan_flags_dpp_operand_written_too_late():
