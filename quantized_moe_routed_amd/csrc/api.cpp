@@ -98,10 +98,11 @@ size_t route_ws_bytes(int T, int E, int H, int fmt = MOE_W_Q8_0) { return align_
 // Expert-forward workspace: tile list, per-token row scales, the fp16
 // activation operand (hi plane; lo plane for fp32 activations) with its block
 // sums, the intermediate h in fp32 with its block sums and block maxima, and,
-// where large tiles can occur, the down projection's fp16 hi + lo operand of
-// their rows with its block sums and row scales.  Block rows are padded to a
-// multiple of 32 blocks.
-constexpr int kLargeTile = 128;   // slots per large tile
+// where large tiles can occur or the batch has more than kSelMaxTokens tokens,
+// the down projection's fp16 hi + lo operand of the tiles' rows with its block
+// sums and row scales (single tokens: the block-scaled planes of h).  Block
+// rows are padded to a multiple of 32 blocks.
+constexpr int kLargeTile = moe::kLargeTileRows;   // slots per large tile
 
 // Fewest slots of an expert that go to large tiles in a batch of T tokens, 0 = small tiles only.
 // Up to 32 tokens an expert fills at most 4 small tiles of 8 and the large-tile launches would run
@@ -168,11 +169,14 @@ FwdLayout fwd_layout(int T, int H, int I, int k, int E_local, int xt) {
   L.h = take(TK * I * 4);
   L.hs = take(TK * nb32I * 4);
   L.hm = take(TK * nb32I * 4);
-  if (tp.max_large > 0 || T == 1) {   // large tiles' operand; one-slot tiles' block-scaled planes
+  // the down projection's prepared operand: of the large tiles' rows and, past kSelMaxTokens
+  // tokens, of the small tiles' rows (one-slot tiles: their block-scaled planes)
+  const bool prep = tp.max_large > 0 || T > moe::kSelMaxTokens;
+  if (prep || T == 1) {
     L.hq_hi = take(TK * I * 2);
     L.hq_lo = take(TK * I * 2);
   }
-  if (tp.max_large > 0) {
+  if (prep) {
     L.hsq_hi = take(TK * nb32I * 2);
     L.hsq_lo = take(TK * nb32I * 2);
     L.hsig = take(TK * sizeof(float));
@@ -421,11 +425,12 @@ moe_status forward_setup(const char* fn, const void* x, int32_t xt, int32_t T, i
   a.h = atf(L.h);
   a.hs = atf(L.hs);
   a.hm = atf(L.hm);
-  if (tp.max_large > 0 || T == 1) {
+  const bool prep = tp.max_large > 0 || T > moe::kSelMaxTokens;   // (as fwd_layout)
+  if (prep || T == 1) {
     a.hq_hi = at16(L.hq_hi);
     a.hq_lo = at16(L.hq_lo);
   }
-  if (tp.max_large > 0) {
+  if (prep) {
     a.hsq_hi = at16(L.hsq_hi);
     a.hsq_lo = at16(L.hsq_lo);
     a.hsig = atf(L.hsig);

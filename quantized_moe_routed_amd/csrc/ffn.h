@@ -86,6 +86,6 @@ struct HConvArgs {
   const int32_t* n_tiles;
   int I, nb32I;
 };
-hipError_t launch_hconv(const HConvArgs& c, int max_tiles, hipStream_t s);
+hipError_t launch_hconv(const HConvArgs& c, int max_tiles, int max_rows, hipStream_t s);   // max_rows: per tile
 
 }  // namespace moe

@@ -64,10 +64,13 @@ __host__ __device__ constexpr size_t one_red_offset(bool sel, int stage_rows, in
 
 
 
-template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL>
+// PRE (down of several slots): the operand rows come prepared (the conversion launch wrote each row
+// of h scaled and split, with its block sums and row scale), staged as they are; without PRE each
+// wave converts its own range of the fp32 rows while staging (CONV).
+template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL, bool PRE = false>
 __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a) {
   constexpr int UB = Codes<F>::kUnitBlocks;
-  constexpr bool CONV = MODE == MODE_DOWN && !ONE;   // down of several slots: converts fp32 h while staging
+  constexpr bool CONV = MODE == MODE_DOWN && !ONE && !PRE;   // down of several slots: converts fp32 h while staging
   constexpr bool BSC = MODE == MODE_DOWN && ONE;     // down of one slot: block-scaled operand planes
   constexpr int CH = NM == 2 ? 2 : (F == FMT_Q8_0 ? 4 : 1);   // units whose loads are issued together
   extern __shared__ __align__(16) uint8_t smem[];
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   uint16_t* st_hi = reinterpret_cast<uint16_t*>(smem);
   uint16_t* st_lo = st_hi + a.stage_rows * K;
   uint16_t* st_zero = st_lo + (LO ? a.stage_rows * K : 0);   // one row of zeros for rows without a slot
-  if constexpr (MODE == MODE_GATEUP)
+  if constexpr (MODE == MODE_GATEUP || PRE)   // the rows' scales (prepared down operand: per grouped position)
     if (tid < kStageRows) s_sig[tid] = tid < rows ? a.sigma[row_of(tid)] : 1.0f;
   const int k0 = 32 * UB * u_beg, k1 = min(32 * UB * u_end, K);
   for (int e = k0 + 8 * lane; e < k1; e += 8 * kWave)
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
       sv = sin ? (c16 < 8 ? hi : lo) : zero;
     }
   };
-  if constexpr (Codes<F>::kHasM && MODE == MODE_GATEUP) load_s(u_beg);
+  if constexpr (Codes<F>::kHasM && (MODE == MODE_GATEUP || PRE)) load_s(u_beg);   // (CONV: after converting)
   load_chunk(u_beg);
   // nothing that uses a loaded value is scheduled among the loads above: no wait delays their issue
   __builtin_amdgcn_sched_barrier(0);
@@ -537,7 +540,8 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   const bool owner = tid < 16 * kStageRows;
   const int lhi = 16 * ((m >> 2) & 1) + l, llo = lhi + 32, cm = m & 3;
   if constexpr (MODE == MODE_DOWN) {
-    const float inv = 1.0f / __shfl(sig, (m & 7) * (kWave / kStageRows), kWave);   // a power of two: exact
+    // the row's scale: converted here (CONV) or prepared (a power of two either way: exact)
+    const float inv = PRE ? 1.0f / s_sig[m & 7] : 1.0f / __shfl(sig, (m & 7) * (kWave / kStageRows), kWave);
     if (owner && m < rows) {
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
@@ -591,7 +595,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   }
 }
 
-template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL = false>
+template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL = false, bool PRE = false>
 static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_t s) {
   const size_t stage = (size_t)t.stage_rows * t.K * 2 * (LO ? 2 : 1) + (size_t)t.K * 2;
   const size_t red = (size_t)kFfnWaves * kNT * NM * 4 * kWave * 4 + kStageRows * 33 * 4;
@@ -602,7 +606,7 @@ static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_
     if (lds < one) lds = one;
   }
 
-  auto kern = ffn_small_kernel<F, NM, LO, MODE, ONE, SEL>;
+  auto kern = ffn_small_kernel<F, NM, LO, MODE, ONE, SEL, PRE>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -657,13 +661,24 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
     trace_post("ffn_gateup_large", s);
     if (err != hipSuccess) return err;
   }
-  // the large tiles' rows of h as the down projection's prepared operand
+  // the rows of h as the down projection's prepared operand: the large tiles' rows, and for batches
+  // of more than kSelMaxTokens tokens the small tiles' rows too (converted once per row instead of
+  // in each of a tile's column workgroups)
+  const bool pre = a.T > kSelMaxTokens;
   if (a.max_large > 0) {
     const HConvArgs c{a.h, a.hs, a.hm, a.hq_hi, a.hq_lo, a.hsq_hi, a.hsq_lo, a.hsig, a.large, a.n_large, a.I,
                       a.nb32I};
     trace_pre("hconv", s);
-    err = launch_hconv(c, a.max_large, s);
+    err = launch_hconv(c, a.max_large, kLargeTileRows, s);
     trace_post("hconv", s);
+    if (err != hipSuccess) return err;
+  }
+  if (pre) {
+    const HConvArgs c{a.h, a.hs, a.hm, a.hq_hi, a.hq_lo, a.hsq_hi, a.hsq_lo, a.hsig, a.small, a.n_small, a.I,
+                      a.nb32I};
+    trace_pre("hconv_small", s);
+    err = launch_hconv(c, a.max_small, a.bm_small, s);
+    trace_post("hconv_small", s);
     if (err != hipSuccess) return err;
   }
   // down: h (hi + lo) x down  ->  y_slot; small tiles scale and split their rows of h themselves
@@ -673,7 +688,11 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   t.y = a.y;
   t.tiles = a.small; t.n_tiles = a.n_small;
   trace_pre("ffn_down", s, true);
-  err = a.fd == FMT_Q2SM ? MOE_SMALL(FMT_Q2SM, 1, true, MODE_DOWN) : MOE_SMALL(FMT_Q8_0, 1, true, MODE_DOWN);
+  if (pre)
+    err = a.fd == FMT_Q2SM ? launch_small_t<FMT_Q2SM, 1, true, MODE_DOWN, false, false, true>(t, a.max_small, s)
+                           : launch_small_t<FMT_Q8_0, 1, true, MODE_DOWN, false, false, true>(t, a.max_small, s);
+  else
+    err = a.fd == FMT_Q2SM ? MOE_SMALL(FMT_Q2SM, 1, true, MODE_DOWN) : MOE_SMALL(FMT_Q8_0, 1, true, MODE_DOWN);
   trace_post("ffn_down", s);
   if (err != hipSuccess) return err;
   if (a.max_large > 0) {

@@ -521,7 +521,8 @@ static hipError_t launch_large_t(const FfnTileArgs& t, int max_tiles, hipStream_
   return launch_stamped(ffn_large_kernel<F, NM, LO, MODE, NT2, WM, CG>, dim3(grid), dim3(C::THREADS), lds, s, t, n_ct);
 }
 
-// The down projection's operand of the rows of the large tiles.  Workgroup (tile, q) takes rows
+// The down projection's operand of the rows of a tile list (the large tiles; for batches of more
+// than kSelMaxTokens tokens the small tiles too).  Workgroup (tile, q) takes rows
 // 8 q .. 8 q + 7 of the tile, a wave per row: the row's scale from its block maxima (row_scale, the
 // rule of the activation operand), then h times 2^6 sigma and the block sums times sigma as fp16
 // hi + lo pairs.  Each row is read and written once.
@@ -558,8 +559,8 @@ __global__ __launch_bounds__(kConvWaves * kWave) void hconv_kernel(HConvArgs c) 
   }
 }
 
-hipError_t launch_hconv(const HConvArgs& c, int max_tiles, hipStream_t s) {
-  hconv_kernel<<<dim3(max_tiles, kLgRows / kConvWaves), kConvWaves * kWave, 0, s>>>(c);
+hipError_t launch_hconv(const HConvArgs& c, int max_tiles, int max_rows, hipStream_t s) {
+  hconv_kernel<<<dim3(max_tiles, (max_rows + kConvWaves - 1) / kConvWaves), kConvWaves * kWave, 0, s>>>(c);
   return hipGetLastError();
 }
 

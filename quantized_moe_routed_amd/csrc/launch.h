@@ -116,6 +116,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 // workgroups share a compute unit, for gate/up (K = H; hi and lo planes for fp32 activations) and
 // for down (K = I, hi and lo planes), else 4.
 constexpr int kSmallRowsMax = 8;
+constexpr int kLargeTileRows = 128;   // slots per large tile
 int small_tile_rows(int H, int I, bool f32_act);
 
 hipError_t launch_combine(const float* y, const float* w, const int32_t* ids, const int32_t* g2l, int T, int k,
