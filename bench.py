@@ -445,10 +445,13 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    copy_gbs = None
     if args.calibration_copy:
+        # (a counter run: the only large copy is the calibration one, which scales the counters)
         calibration_copy(torch)
-    copy_gbs = copy_ceiling_gbs(torch)
-    log(f"device copy: {copy_gbs:.0f} GB/s (read + write)")
+    else:
+        copy_gbs = copy_ceiling_gbs(torch)
+        log(f"device copy: {copy_gbs:.0f} GB/s (read + write)")
     wl, head = measure(args.workload, args.steps, args.warmup, torch, copy_gbs)
     others = {}
     if not args.only:
