@@ -636,71 +636,88 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   t.h = a.h; t.hs = a.hs; t.hm = a.hm; t.hb_hi = a.hq_hi; t.hb_lo = a.hq_lo;
   const bool lo = a.xq_lo != nullptr;
   const bool one = a.T == 1;
-#define MOE_SMALL(F, NM, LO, MODE) \
-  (one ? launch_small_t<F, NM, LO, MODE, true>(t, a.max_small, s) : launch_small_t<F, NM, LO, MODE, false>(t, a.max_small, s))
+#define MOE_SMALL(F, NM, LO, MODE, S) \
+  (one ? launch_small_t<F, NM, LO, MODE, true>(t, a.max_small, S) : launch_small_t<F, NM, LO, MODE, false>(t, a.max_small, S))
 #define MOE_SMALL_SEL(F, LO)                                                                        \
-  (one ? launch_small_t<F, 2, LO, MODE_GATEUP, true, true>(t, a.max_small, s)                       \
-       : launch_small_t<F, 2, LO, MODE_GATEUP, false, true>(t, a.max_small, s))
+  (one ? launch_small_t<F, 2, LO, MODE_GATEUP, true, true>(t, a.max_small, ss)                      \
+       : launch_small_t<F, 2, LO, MODE_GATEUP, false, true>(t, a.max_small, ss))
+  // The small tiles (their gate/up, the conversion of their rows of h, their down) and the large
+  // tiles (the same three) touch disjoint rows of h and of y: with a second stream the two chains
+  // run concurrently, the small tiles' streaming of the light experts' weights beside the large
+  // tiles' matrix work.
+  const bool fork = a.max_large > 0 && a.side;
+  const hipStream_t ss = fork ? a.side : s;
+  if (fork) {
+    if ((err = hipEventRecord(a.fork, s)) != hipSuccess) return err;
+    if ((err = hipStreamWaitEvent(ss, a.fork, 0)) != hipSuccess) return err;
+  }
+  // the rows of h as the down projection's prepared operand: the large tiles' rows, and for batches
+  // of more than kSelMaxTokens tokens the small tiles' rows too (converted once per row instead of
+  // in each of a tile's column workgroups)
+  const bool pre = a.T > kSelMaxTokens;
+  FfnTileArgs d = t;   // down: h (hi + lo) x down  ->  y_slot
+  d.a_hi = a.hq_hi; d.a_lo = a.hq_lo; d.s_hi = a.hsq_hi; d.s_lo = a.hsq_lo; d.sigma = a.hsig;
+  d.hf = a.h; d.hsf = a.hs; d.hmf = a.hm;
+  d.K = a.I; d.N = a.H; d.nb32 = a.nb32I; d.w0 = a.down; d.w1 = a.down;
+  d.y = a.y;
+
+  // small tiles: gate/up, [conversion,] down (small tiles without the conversion scale and split
+  // their rows of h themselves)
   t.tiles = a.small; t.tile_tok = a.small_tok; t.n_tiles = a.n_small;
-  trace_pre("ffn_gateup", s, true);
+  trace_pre("ffn_gateup", ss, true);
   if (a.sel) {
     t.sel = *a.sel;
     if (a.fg == FMT_Q2SM) err = lo ? MOE_SMALL_SEL(FMT_Q2SM, true) : MOE_SMALL_SEL(FMT_Q2SM, false);
     else err = lo ? MOE_SMALL_SEL(FMT_Q8_0, true) : MOE_SMALL_SEL(FMT_Q8_0, false);
   } else if (a.fg == FMT_Q2SM) {
-    err = lo ? MOE_SMALL(FMT_Q2SM, 2, true, MODE_GATEUP) : MOE_SMALL(FMT_Q2SM, 2, false, MODE_GATEUP);
+    err = lo ? MOE_SMALL(FMT_Q2SM, 2, true, MODE_GATEUP, ss) : MOE_SMALL(FMT_Q2SM, 2, false, MODE_GATEUP, ss);
   } else {
-    err = lo ? MOE_SMALL(FMT_Q8_0, 2, true, MODE_GATEUP) : MOE_SMALL(FMT_Q8_0, 2, false, MODE_GATEUP);
+    err = lo ? MOE_SMALL(FMT_Q8_0, 2, true, MODE_GATEUP, ss) : MOE_SMALL(FMT_Q8_0, 2, false, MODE_GATEUP, ss);
   }
-  trace_post("ffn_gateup", s);
+  trace_post("ffn_gateup", ss);
   if (err != hipSuccess) return err;
+  if (pre) {
+    const HConvArgs c{a.h, a.hs, a.hm, a.hq_hi, a.hq_lo, a.hsq_hi, a.hsq_lo, a.hsig, a.small, a.n_small, a.I,
+                      a.nb32I};
+    trace_pre("hconv_small", ss);
+    err = launch_hconv(c, a.max_small, a.bm_small, ss);
+    trace_post("hconv_small", ss);
+    if (err != hipSuccess) return err;
+  }
+  d.tiles = a.small; d.n_tiles = a.n_small;
+  {
+    const FfnTileArgs& t = d;   // (the launch macros take t)
+    trace_pre("ffn_down", ss, true);
+    if (pre)
+      err = a.fd == FMT_Q2SM ? launch_small_t<FMT_Q2SM, 1, true, MODE_DOWN, false, false, true>(t, a.max_small, ss)
+                             : launch_small_t<FMT_Q8_0, 1, true, MODE_DOWN, false, false, true>(t, a.max_small, ss);
+    else
+      err = a.fd == FMT_Q2SM ? MOE_SMALL(FMT_Q2SM, 1, true, MODE_DOWN, ss) : MOE_SMALL(FMT_Q8_0, 1, true, MODE_DOWN, ss);
+    trace_post("ffn_down", ss);
+    if (err != hipSuccess) return err;
+  }
+  if (fork && (err = hipEventRecord(a.join, ss)) != hipSuccess) return err;
+
+  // large tiles: gate/up, conversion, down
   if (a.max_large > 0) {
     t.tiles = a.large; t.n_tiles = a.n_large;
     trace_pre("ffn_gateup_large", s, true);
     err = launch_large(t, a.fg, MODE_GATEUP, lo, a.max_large, s);
     trace_post("ffn_gateup_large", s);
     if (err != hipSuccess) return err;
-  }
-  // the rows of h as the down projection's prepared operand: the large tiles' rows, and for batches
-  // of more than kSelMaxTokens tokens the small tiles' rows too (converted once per row instead of
-  // in each of a tile's column workgroups)
-  const bool pre = a.T > kSelMaxTokens;
-  if (a.max_large > 0) {
     const HConvArgs c{a.h, a.hs, a.hm, a.hq_hi, a.hq_lo, a.hsq_hi, a.hsq_lo, a.hsig, a.large, a.n_large, a.I,
                       a.nb32I};
     trace_pre("hconv", s);
     err = launch_hconv(c, a.max_large, kLargeTileRows, s);
     trace_post("hconv", s);
     if (err != hipSuccess) return err;
-  }
-  if (pre) {
-    const HConvArgs c{a.h, a.hs, a.hm, a.hq_hi, a.hq_lo, a.hsq_hi, a.hsq_lo, a.hsig, a.small, a.n_small, a.I,
-                      a.nb32I};
-    trace_pre("hconv_small", s);
-    err = launch_hconv(c, a.max_small, a.bm_small, s);
-    trace_post("hconv_small", s);
+    d.tiles = a.large; d.n_tiles = a.n_large;
+    trace_pre("ffn_down_large", s, true);
+    err = launch_large(d, a.fd, MODE_DOWN, true, a.max_large, s);
+    trace_post("ffn_down_large", s);
     if (err != hipSuccess) return err;
   }
-  // down: h (hi + lo) x down  ->  y_slot; small tiles scale and split their rows of h themselves
-  t.a_hi = a.hq_hi; t.a_lo = a.hq_lo; t.s_hi = a.hsq_hi; t.s_lo = a.hsq_lo; t.sigma = a.hsig;
-  t.hf = a.h; t.hsf = a.hs; t.hmf = a.hm;
-  t.K = a.I; t.N = a.H; t.nb32 = a.nb32I; t.w0 = a.down; t.w1 = a.down;
-  t.y = a.y;
-  t.tiles = a.small; t.n_tiles = a.n_small;
-  trace_pre("ffn_down", s, true);
-  if (pre)
-    err = a.fd == FMT_Q2SM ? launch_small_t<FMT_Q2SM, 1, true, MODE_DOWN, false, false, true>(t, a.max_small, s)
-                           : launch_small_t<FMT_Q8_0, 1, true, MODE_DOWN, false, false, true>(t, a.max_small, s);
-  else
-    err = a.fd == FMT_Q2SM ? MOE_SMALL(FMT_Q2SM, 1, true, MODE_DOWN) : MOE_SMALL(FMT_Q8_0, 1, true, MODE_DOWN);
-  trace_post("ffn_down", s);
-  if (err != hipSuccess) return err;
-  if (a.max_large > 0) {
-    t.tiles = a.large; t.n_tiles = a.n_large;
-    trace_pre("ffn_down_large", s, true);
-    err = launch_large(t, a.fd, MODE_DOWN, true, a.max_large, s);
-    trace_post("ffn_down_large", s);
-  }
+  if (fork && (err = hipStreamWaitEvent(s, a.join, 0)) != hipSuccess) return err;
 #undef MOE_SMALL_SEL
 #undef MOE_SMALL
   return err;

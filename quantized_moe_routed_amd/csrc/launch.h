@@ -102,6 +102,11 @@ struct FfnArgs {
   // logits (batches of at most kSelMaxTokens tokens, no large tiles) and stores the routing
   // results; small, small_tok and n_small are then its outputs
   const SelArgs* sel;
+  // non-NULL with large tiles: the small tiles' launches run on this second stream of the device,
+  // concurrently with the large tiles' (fork: recorded on the caller's stream before them, join:
+  // recorded on the second stream after them and waited for by the caller's stream)
+  hipStream_t side;
+  hipEvent_t fork, join;
 };
 
 // Tile lists + fp16 activation operand (fmt.h) in one launch.
