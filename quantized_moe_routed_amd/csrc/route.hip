@@ -484,6 +484,68 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     topk_token<EPL>(z, S, bias, T, E, k, t, ids, w, nullptr, tk_cand + (size_t)(threadIdx.x / kWave) * (E + kThrMaxK));
 }
 
+// Many partial ranges (S >= 16): a workgroup of 4 waves per token.  Wave q adds its quarter of the
+// M ranges (M the power of two that holds S) by the lower levels of the pairwise tree, exactly as
+// logit_keys does for those indices, and leaves the quarter sums in LDS; wave 0 adds the quarters by
+// the tree's two top levels, then the bias, and selects as topk_lanes.  The same additions in the
+// same order: the same keys, and the loads of a token spread over four waves instead of one.
+constexpr int kSplitWaves = 4;
+
+template <int EPL, int M>
+__global__ __launch_bounds__(kSplitWaves * kWave) void route_topk_split_kernel(const float* __restrict__ z, int S,
+                                                                               const float* __restrict__ bias, int T,
+                                                                               int E, int k, int32_t* __restrict__ ids,
+                                                                               float* __restrict__ w) {
+  static_assert(M % kSplitWaves == 0, "whole quarters");
+  constexpr int G = M / kSplitWaves;   // ranges per wave
+  __shared__ float qs[kSplitWaves][EPL * kWave];
+  __shared__ uint64_t cand[EPL * kWave + kThrMaxK];
+  const int t = blockIdx.x, lane = threadIdx.x % kWave;
+  const int q = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  int ec[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) ec[i] = min(i * kWave + lane, E - 1);
+  {
+    float v[EPL][G];
+#pragma unroll
+    for (int jj = 0; jj < G; ++jj) {
+      const float* zj = z + ((int64_t)min(q * G + jj, S - 1) * T + t) * E;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) v[i][jj] = zj[ec[i]];
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+#pragma unroll
+      for (int wd = 1; wd < G; wd <<= 1)
+#pragma unroll
+        for (int jj = 0; jj + wd < G; jj += 2 * wd) {
+          const int j = q * G + jj;   // the pair's left index in the whole tree
+          v[i][jj] = j + wd < S ? v[i][jj] + v[i][jj + wd] : v[i][jj];
+        }
+      qs[q][i * kWave + lane] = v[i][0];
+    }
+  }
+  __syncthreads();
+  if (q != 0) return;
+  uint32_t key[EPL];
+  bool live[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    live[i] = i * kWave + lane < E;
+    const float bv = bias ? bias[ec[i]] : 0.0f;
+    const float a0 = qs[0][i * kWave + lane], a1 = qs[1][i * kWave + lane];
+    const float a2 = qs[2][i * kWave + lane], a3 = qs[3][i * kWave + lane];
+    const float l = G < S ? a0 + a1 : a0;            // pair (0, G)
+    const float r = 3 * G < S ? a2 + a3 : a2;        // pair (2G, 3G)
+    const float zs = 2 * G < S ? l + r : l;          // pair (0, 2G)
+    key[i] = live[i] ? float_key(bias ? zs + bv : zs) : 0u;
+  }
+  int my_id;
+  uint32_t my_key;
+  topk_of_keys<EPL>(key, live, E, k, lane, cand, my_id, my_key);
+  if (w) topk_store(k, t, my_id, my_key, ids, w);
+}
+
 template <int ACT>
 static hipError_t launch_logits_c(int C, const void* x, int T, int H, const QMat& r, const float* bias,
                                   float* z, const PrepOut& po, hipStream_t s) {
@@ -597,6 +659,13 @@ hipError_t launch_route(const void* x, int act, int T, int H, int fmt, const QMa
   hipError_t err = launch_logits(x, act, T, H, fmt, router, bias, ws, &S, s, nullptr);
   if (err != hipSuccess) return err;
   const float* z = reinterpret_cast<const float*>(ws);
+  if (S >= 16 && E <= 256) {   // the ranges of a token over four waves
+    trace_pre("route_topk", s);
+    if (S <= 16) route_topk_split_kernel<4, 16><<<T, kSplitWaves * kWave, 0, s>>>(z, S, bias, T, E, k, ids, w);
+    else route_topk_split_kernel<4, 32><<<T, kSplitWaves * kWave, 0, s>>>(z, S, bias, T, E, k, ids, w);
+    trace_post("route_topk", s);
+    return hipGetLastError();
+  }
   dim3 grid((T + 3) / 4);
   const size_t lds = (size_t)4 * (E + kThrMaxK) * sizeof(uint64_t);   // (at most 33 KiB: E <= 1024)
   trace_pre("route_topk", s);

@@ -184,6 +184,10 @@ __device__ __forceinline__ void topk_threshold(const uint32_t (&key)[EPL], const
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // cand is free again for the next call
 }
 
+template <int EPL>
+__device__ __forceinline__ void topk_of_keys(uint32_t (&key)[EPL], bool (&live)[EPL], int E, int k, int lane,
+                                             uint64_t* cand, int& my_id, uint32_t& my_key);
+
 // One wave per token: k rounds, each one wave maximum of (logit key, complement of the expert
 // index) over the untaken experts, i.e. the largest logit with ties to the lower index.
 // Weights: s_j = sigmoid(z_j) in fp64 on lane j, their sum taken in slot order by every lane,
@@ -200,6 +204,13 @@ __device__ __forceinline__ void topk_lanes(const float* __restrict__ z, int S, c
   bool live[EPL];
   if (S == 0) logit_keys<EPL, 0>(z, S, bias, T, E, t, lane, key, live);
   else logit_keys_upto<EPL, 4, MAXS>(z, S, bias, T, E, t, lane, key, live);
+  topk_of_keys<EPL>(key, live, E, k, lane, cand, my_id, my_key);
+}
+
+// The selection of topk_lanes from the lanes' keys (all lanes of the wave take part).
+template <int EPL>
+__device__ __forceinline__ void topk_of_keys(uint32_t (&key)[EPL], bool (&live)[EPL], int E, int k, int lane,
+                                             uint64_t* cand, int& my_id, uint32_t& my_key) {
   my_id = -1;
   my_key = 0;
   if (cand && k <= kThrMaxK) {
