@@ -1,5 +1,5 @@
-// Grouping of routing slots by expert: the one-workgroup counting sort of
-// group.h as a launch of its own.
+// Grouping of routing slots by expert: the counting sort of group.h, one
+// workgroup per chunk of kGroupThreads slots.
 #include "device.h"
 #include "launch.h"
 #include "group.h"
@@ -12,16 +12,18 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
                                                               int32_t* __restrict__ slot_list) {
   extern __shared__ int32_t sm[];
   __shared__ int32_t wave_tot[kGroupWaves];
-  group_block(ids, n, E, nbits, counts, offsets, slot_list, sm, wave_tot);
+  group_chunk(ids, n, E, nbits, blockIdx.x, counts, offsets, slot_list, sm, wave_tot);
 }
 
 hipError_t launch_group(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
                         int32_t* slot_list, hipStream_t s) {
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
+  const int n = T * k;
+  const int chunks = n > 0 ? (n + kGroupThreads - 1) / kGroupThreads : 1;   // (no slots: zero counts and offsets)
   const size_t lds = sizeof(int32_t) * (size_t)(2 + kGroupWaves) * E;
   trace_pre("group", s);
-  group_kernel<<<1, kGroupThreads, lds, s>>>(ids, T * k, E, nbits, counts, offsets, slot_list);
+  group_kernel<<<chunks, kGroupThreads, lds, s>>>(ids, n, E, nbits, counts, offsets, slot_list);
   trace_post("group", s);
   return hipGetLastError();
 }

@@ -366,6 +366,39 @@ def test_topk_ties_against_a_stable_sort(torch, E, k):
         assert_close(got[1].reshape(T, k), np.tile(sg / sg.sum(), (T, 1)), what=f"weights E={E} k={k}")
 
 
+@pytest.mark.parametrize("T,k,E", [(300, 8, 256), (2049, 8, 64), (129, 8, 1024), (4096, 1, 3)])
+def test_group_over_several_chunks(torch, T, k, E):
+    """The grouping launch takes 1024 slots per workgroup: batches of several chunks with a ragged
+    last one, ids outside [0, E) (left out) and experts that receive nothing.  counts, offsets and
+    the slot list equal a stable sort of the valid slots by expert (numpy's stable argsort), and
+    slot_list entries past the valid slots are left untouched."""
+    _say(f"grouping over chunks: T={T} k={k} E={E}")
+    rng = np.random.default_rng(T * 31 + k)
+    n = T * k
+    ids = rng.integers(0, E, size=n).astype(np.int32)
+    ids[rng.random(n) < 0.02] = -1                 # left out
+    ids[rng.random(n) < 0.02] = E + 5              # left out
+    if E >= 64:
+        ids[(ids % 7) == 3] = 0                    # a heavy expert; others receive nothing
+    valid = (ids >= 0) & (ids < E)
+    counts_ref = np.bincount(ids[valid], minlength=E).astype(np.int32)
+    offsets_ref = np.concatenate([[0], np.cumsum(counts_ref)]).astype(np.int32)
+    vs = np.nonzero(valid)[0]
+    order_ref = vs[np.argsort(ids[vs], kind="stable")].astype(np.int32)
+    d = torch.device("cuda")
+    ids_d = torch.from_numpy(ids).to(d)
+    counts = torch.full((E,), -9, dtype=torch.int32, device=d)
+    offsets = torch.full((E + 1,), -9, dtype=torch.int32, device=d)
+    slots = torch.full((n,), -9, dtype=torch.int32, device=d)
+    moe.group_tokens(ids_d, T, k, E, counts, offsets, slots)
+    torch.cuda.synchronize()
+    assert np.array_equal(counts.cpu().numpy(), counts_ref)
+    assert np.array_equal(offsets.cpu().numpy(), offsets_ref)
+    got = slots.cpu().numpy()
+    assert np.array_equal(got[: len(vs)], order_ref)
+    assert np.all(got[len(vs):] == -9)
+
+
 @pytest.mark.parametrize("k", [1, 5, 8, 9, 17])
 def test_combine_alone(torch, k):
     """moe_combine by itself, with and without an owner table (some experts unowned, one id past the
