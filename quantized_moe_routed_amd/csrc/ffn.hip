@@ -663,61 +663,74 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
 
   // small tiles: gate/up, [conversion,] down (small tiles without the conversion scale and split
   // their rows of h themselves)
-  t.tiles = a.small; t.tile_tok = a.small_tok; t.n_tiles = a.n_small;
-  trace_pre("ffn_gateup", ss, true);
-  if (a.sel) {
-    t.sel = *a.sel;
-    if (a.fg == FMT_Q2SM) err = lo ? MOE_SMALL_SEL(FMT_Q2SM, true) : MOE_SMALL_SEL(FMT_Q2SM, false);
-    else err = lo ? MOE_SMALL_SEL(FMT_Q8_0, true) : MOE_SMALL_SEL(FMT_Q8_0, false);
-  } else if (a.fg == FMT_Q2SM) {
-    err = lo ? MOE_SMALL(FMT_Q2SM, 2, true, MODE_GATEUP, ss) : MOE_SMALL(FMT_Q2SM, 2, false, MODE_GATEUP, ss);
-  } else {
-    err = lo ? MOE_SMALL(FMT_Q8_0, 2, true, MODE_GATEUP, ss) : MOE_SMALL(FMT_Q8_0, 2, false, MODE_GATEUP, ss);
-  }
-  trace_post("ffn_gateup", ss);
-  if (err != hipSuccess) return err;
-  if (pre) {
-    const HConvArgs c{a.h, a.hs, a.hm, a.hq_hi, a.hq_lo, a.hsq_hi, a.hsq_lo, a.hsig, a.small, a.n_small, a.I,
-                      a.nb32I};
-    trace_pre("hconv_small", ss);
-    err = launch_hconv(c, a.max_small, a.bm_small, ss);
-    trace_post("hconv_small", ss);
-    if (err != hipSuccess) return err;
-  }
-  d.tiles = a.small; d.n_tiles = a.n_small;
-  {
+  auto small_chain = [&]() -> hipError_t {
+    hipError_t e;
+    t.tiles = a.small; t.tile_tok = a.small_tok; t.n_tiles = a.n_small;
+    trace_pre("ffn_gateup", ss, true);
+    if (a.sel) {
+      t.sel = *a.sel;
+      if (a.fg == FMT_Q2SM) e = lo ? MOE_SMALL_SEL(FMT_Q2SM, true) : MOE_SMALL_SEL(FMT_Q2SM, false);
+      else e = lo ? MOE_SMALL_SEL(FMT_Q8_0, true) : MOE_SMALL_SEL(FMT_Q8_0, false);
+    } else if (a.fg == FMT_Q2SM) {
+      e = lo ? MOE_SMALL(FMT_Q2SM, 2, true, MODE_GATEUP, ss) : MOE_SMALL(FMT_Q2SM, 2, false, MODE_GATEUP, ss);
+    } else {
+      e = lo ? MOE_SMALL(FMT_Q8_0, 2, true, MODE_GATEUP, ss) : MOE_SMALL(FMT_Q8_0, 2, false, MODE_GATEUP, ss);
+    }
+    trace_post("ffn_gateup", ss);
+    if (e != hipSuccess) return e;
+    if (pre) {
+      const HConvArgs c{a.h, a.hs, a.hm, a.hq_hi, a.hq_lo, a.hsq_hi, a.hsq_lo, a.hsig, a.small, a.n_small, a.I,
+                        a.nb32I};
+      trace_pre("hconv_small", ss);
+      e = launch_hconv(c, a.max_small, a.bm_small, ss);
+      trace_post("hconv_small", ss);
+      if (e != hipSuccess) return e;
+    }
+    d.tiles = a.small; d.n_tiles = a.n_small;
     const FfnTileArgs& t = d;   // (the launch macros take t)
     trace_pre("ffn_down", ss, true);
     if (pre)
-      err = a.fd == FMT_Q2SM ? launch_small_t<FMT_Q2SM, 1, true, MODE_DOWN, false, false, true>(t, a.max_small, ss)
-                             : launch_small_t<FMT_Q8_0, 1, true, MODE_DOWN, false, false, true>(t, a.max_small, ss);
+      e = a.fd == FMT_Q2SM ? launch_small_t<FMT_Q2SM, 1, true, MODE_DOWN, false, false, true>(t, a.max_small, ss)
+                           : launch_small_t<FMT_Q8_0, 1, true, MODE_DOWN, false, false, true>(t, a.max_small, ss);
     else
-      err = a.fd == FMT_Q2SM ? MOE_SMALL(FMT_Q2SM, 1, true, MODE_DOWN, ss) : MOE_SMALL(FMT_Q8_0, 1, true, MODE_DOWN, ss);
+      e = a.fd == FMT_Q2SM ? MOE_SMALL(FMT_Q2SM, 1, true, MODE_DOWN, ss) : MOE_SMALL(FMT_Q8_0, 1, true, MODE_DOWN, ss);
     trace_post("ffn_down", ss);
-    if (err != hipSuccess) return err;
-  }
-  if (fork && (err = hipEventRecord(a.join, ss)) != hipSuccess) return err;
-
+    return e;
+  };
   // large tiles: gate/up, conversion, down
-  if (a.max_large > 0) {
+  auto large_chain = [&]() -> hipError_t {
+    if (a.max_large == 0) return hipSuccess;
+    hipError_t e;
     t.tiles = a.large; t.n_tiles = a.n_large;
     trace_pre("ffn_gateup_large", s, true);
-    err = launch_large(t, a.fg, MODE_GATEUP, lo, a.max_large, s);
+    e = launch_large(t, a.fg, MODE_GATEUP, lo, a.max_large, s);
     trace_post("ffn_gateup_large", s);
-    if (err != hipSuccess) return err;
+    if (e != hipSuccess) return e;
     const HConvArgs c{a.h, a.hs, a.hm, a.hq_hi, a.hq_lo, a.hsq_hi, a.hsq_lo, a.hsig, a.large, a.n_large, a.I,
                       a.nb32I};
     trace_pre("hconv", s);
-    err = launch_hconv(c, a.max_large, kLargeTileRows, s);
+    e = launch_hconv(c, a.max_large, kLargeTileRows, s);
     trace_post("hconv", s);
-    if (err != hipSuccess) return err;
+    if (e != hipSuccess) return e;
     d.tiles = a.large; d.n_tiles = a.n_large;
     trace_pre("ffn_down_large", s, true);
-    err = launch_large(d, a.fd, MODE_DOWN, true, a.max_large, s);
+    e = launch_large(d, a.fd, MODE_DOWN, true, a.max_large, s);
     trace_post("ffn_down_large", s);
-    if (err != hipSuccess) return err;
+    return e;
+  };
+  err = small_chain();
+  if (fork) {
+    // the join, also after a failed launch: the caller's stream must not run ahead of what the
+    // second stream already holds (if the join cannot be recorded, the host waits for that stream)
+    hipError_t ej = hipEventRecord(a.join, ss);
+    const hipError_t el = err == hipSuccess ? large_chain() : hipSuccess;
+    if (ej == hipSuccess) ej = hipStreamWaitEvent(s, a.join, 0);
+    if (ej != hipSuccess) (void)hipStreamSynchronize(ss);
+    if (err == hipSuccess) err = el;
+    if (err == hipSuccess) err = ej;
+  } else if (err == hipSuccess) {
+    err = large_chain();
   }
-  if (fork && (err = hipStreamWaitEvent(s, a.join, 0)) != hipSuccess) return err;
 #undef MOE_SMALL_SEL
 #undef MOE_SMALL
   return err;
