@@ -223,6 +223,12 @@ moe_status moe_group_tokens(const int32_t* ids, int32_t T, int32_t k, int32_t E,
  * (block's) largest keeps 22 significant bits, smaller ones an absolute error
  * below 2^-39 of that largest, and any finite input is in range.  No path
  * uses floating-point atomics; results do not depend on scheduling.
+ * From 256 tokens, when some expert takes large tiles, the launches of the
+ * small tiles run on a second stream of the device, created by the library on
+ * the device's first such call (not while s is being captured) and held until
+ * the process ends; they are forked from s and joined back into s with events,
+ * so the call stays ordered on s as a whole, and a graph captured from s holds
+ * both branches.  The calls on one device share that stream.
  * Limits: H and I multiples of 32, H <= 8192, I <= 8192. */
 moe_status moe_expert_forward(const void* x, int32_t xt, int32_t T, int32_t H, int32_t I, int32_t k,
                               const moe_experts* local, const int32_t* g2l, int32_t E, int32_t E_local,
@@ -241,9 +247,10 @@ moe_status moe_combine(const float* y_slot, const float* w, const int32_t* ids, 
 /* The whole layer in one call: moe_route, moe_group_tokens, moe_expert_forward
  * and moe_combine in turn on stream s, with their arguments and outputs (ids,
  * w, counts, offsets, slot_list, y_slot, out) and the same results bit for bit;
- * router->rows must equal E.  For batches of up to 8 tokens, the top-k
- * selection, the grouping, the tile lists and the activation operands are
- * produced by a single launch after the logits.
+ * router->rows must equal E.  For batches of up to 8 tokens the logits launch
+ * also prepares the activation operand, and the gate/up launch itself takes
+ * the top-k, groups the slots and numbers the tiles (more than 256 experts:
+ * one launch between the two does so).
  *   ws : route_ws + forward_ws bytes from moe_workspace_size, the router's part
  *        first (route_ws is a multiple of 256), 16-byte aligned.
  * All arguments are checked before the first launch; errors as for the four
