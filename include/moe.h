@@ -266,7 +266,9 @@ moe_status moe_layer_forward(const void* x, int32_t xt, int32_t T, int32_t H, in
  * allocate device memory (code being captured into a HIP graph, tight serving
  * loops, harnesses that forbid allocation).  The workspace is a 32 MiB array
  * the library holds on each device from the moment it is loaded there until
- * the process ends; this call allocates nothing.  Every call on a device uses
+ * the process ends; this call allocates nothing (it forks onto the second
+ * stream of large batches, see moe_expert_forward, only where an earlier call
+ * created that stream, and otherwise runs on s alone).  Every call on a device uses
  * that device's one array, so calls that overlap on one device (on different
  * streams, or from different threads) race; the array keeps the last call's
  * contents, none of which a later call reads before writing it.  A batch whose

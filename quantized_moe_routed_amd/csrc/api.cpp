@@ -501,12 +501,14 @@ SideStream g_side[kMaxSideDevices];
 std::mutex g_side_init_mu;
 
 // The device's side stream, NULL where there is none: not created while the caller's stream is
-// being captured into a graph (creation is no stream operation), or failed to be created.
+// being captured into a graph (creation is no stream operation), nor by the call without
+// allocation (creating a stream allocates), or failed to be created.
 SideStream* side_of(int dev, hipStream_t s) {
   if (dev < 0 || dev >= kMaxSideDevices) return nullptr;
   SideStream& sd = g_side[dev];
   std::lock_guard<std::mutex> lk(g_side_init_mu);
   if (sd.tried) return sd.s ? &sd : nullptr;
+  if (g_ws_is_scratch) return nullptr;   // (a stream created by an earlier call is used)
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
     (void)hipGetLastError();

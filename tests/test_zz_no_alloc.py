@@ -57,6 +57,32 @@ def test_noalloc_equals_layer_call_twice(torch, cfg, T1, T2):
         check_against_oracle(wl, got, oracle_expect(wl, tokens=tok), what=f"noalloc cfg{cfg} T={T}")
 
 
+def test_noalloc_large_tiles_first(torch):
+    """A batch of 300 tokens with large tiles at small shapes (it fits the scratch array): the call
+    without allocation runs first (in a fresh process no second stream exists yet, and this call
+    does not create one), then the layer call; both give the same results bit for bit."""
+    from quantized_moe_routed_amd.layer import act_code
+    T = 300
+    _say(f"noalloc with large tiles first: T={T}")
+    wl = synth.make(synth.custom(T, 128, 4, 128, 2, bias="zipf1.1", gate_fmt=2, up_fmt=2, down_fmt=1, router_fmt=1,
+                                 act="f32", name="noalloc_t300"))
+    layer = make_layer(wl)
+    x = x_tensor(wl, torch)
+    res = []
+    for noalloc in (True, False):
+        b = layer.buffers(T, act_code(x))
+        b.out.fill_(float("nan"))
+        (layer.run_noalloc if noalloc else layer.run)(x, b)
+        torch.cuda.synchronize()
+        res.append(_outputs(b, T, wl.k))
+    got, ref = res
+    counts = got["counts"]
+    lmin = moe.large_tile_min(T)
+    assert counts.max() >= lmin and ((counts > 0) & (counts < lmin)).any()   # both tile kinds
+    for name in ref:
+        assert np.array_equal(ref[name].view(np.uint8), got[name].view(np.uint8)), f"{name} differs"
+
+
 def test_noalloc_share_and_refusal(torch):
     """An owned share (g2l table) gives the layer call's partial bit for bit; a batch whose workspace
     exceeds the scratch array is refused before anything runs, and its outputs stay untouched."""
