@@ -116,6 +116,7 @@ int64_t max_tiles(int64_t slots, int64_t experts, int bm) { return (slots + bm -
 // Tile-list bounds for T tokens (an expert receives at most T slots).
 struct TilePlan {
   int large_min, bm_small, max_small, max_large;
+  int bm_down, max_down;   // max_down > 0: the down projection's own small tiles of bm_down slots
 };
 
 TilePlan tile_plan(int T, int H, int I, int k, int E_local, int xt) {
@@ -135,13 +136,25 @@ TilePlan tile_plan(int T, int H, int I, int k, int E_local, int xt) {
     p.max_small = (int)std::min<int64_t>(p.max_small, std::min<int64_t>(E_local, slots) *
                                                           ((lmin - 1 + p.bm_small - 1) / p.bm_small));
   p.max_large = large ? (int)max_tiles(slots, std::min<int64_t>(E_local, slots / lmin), kLargeTile) : 0;
+  // past kSelMaxTokens tokens the down projection stages prepared rows, and where its staging (K = I)
+  // holds more slots than the gate/up's (K = H, fp32 activations), its small tiles take that many:
+  // an expert of 5-8 slots then streams its down weights once instead of on two tiles
+  p.bm_down = p.bm_small;
+  p.max_down = 0;
+  const int bmd = moe::small_down_tile_rows(I);
+  if (T > moe::kSelMaxTokens && bmd > p.bm_small) {
+    p.bm_down = bmd;
+    p.max_down = (int)max_tiles(slots, std::min<int64_t>(E_local, slots), bmd);
+    if (large)
+      p.max_down = (int)std::min<int64_t>(p.max_down, std::min<int64_t>(E_local, slots) * ((lmin - 1 + bmd - 1) / bmd));
+  }
   return p;
 }
 
 int pad32(int nb) { return (nb + 31) / 32 * 32; }
 
 struct FwdLayout {
-  size_t n_small, n_large, small, small_tok, large, sigma, xq_hi, xq_lo, sq_hi, sq_lo, h, hs, hm;
+  size_t n_small, n_large, n_down, small, small_tok, down, large, sigma, xq_hi, xq_lo, sq_hi, sq_lo, h, hs, hm;
   size_t hq_hi, hq_lo, hsq_hi, hsq_lo, hsig, total;
 };
 
@@ -160,6 +173,8 @@ FwdLayout fwd_layout(int T, int H, int I, int k, int E_local, int xt) {
   L.n_large = take(sizeof(int32_t));
   L.small = take((size_t)tp.max_small * 4 * sizeof(int32_t));
   L.small_tok = take((size_t)tp.max_small * moe::kSmallRowsMax * sizeof(int32_t));
+  L.n_down = take(tp.max_down > 0 ? sizeof(int32_t) : 0);
+  L.down = take((size_t)tp.max_down * 4 * sizeof(int32_t));
   L.large = take((size_t)tp.max_large * 4 * sizeof(int32_t));
   L.sigma = take((size_t)T * sizeof(float));
   L.xq_hi = take((size_t)T * H * 2);
@@ -417,6 +432,12 @@ moe_status forward_setup(const char* fn, const void* x, int32_t xt, int32_t T, i
   a.n_large = reinterpret_cast<const int32_t*>(wsb + L.n_large);
   a.max_small = tp.max_small;
   a.bm_small = tp.bm_small;
+  if (tp.max_down > 0) {
+    a.down_small = reinterpret_cast<const int4*>(wsb + L.down);
+    a.n_down_small = reinterpret_cast<const int32_t*>(wsb + L.n_down);
+    a.max_down_small = tp.max_down;
+    a.bm_down_small = tp.bm_down;
+  }
   a.max_large = tp.max_large;
   a.xq_hi = at16(L.xq_hi);
   a.xq_lo = xt == MOE_ACT_F32 ? at16(L.xq_lo) : nullptr;
@@ -458,6 +479,12 @@ moe_status forward_setup(const char* fn, const void* x, int32_t xt, int32_t T, i
   tl.large = reinterpret_cast<int4*>(wsb + L.large);
   tl.n_small = reinterpret_cast<int32_t*>(wsb + L.n_small);
   tl.n_large = reinterpret_cast<int32_t*>(wsb + L.n_large);
+  if (tp.max_down > 0) {
+    tl.down = reinterpret_cast<int4*>(wsb + L.down);
+    tl.n_down = reinterpret_cast<int32_t*>(wsb + L.n_down);
+    tl.bm_down = tp.bm_down;
+    tl.max_down = tp.max_down;
+  }
   return MOE_OK;
 }
 

@@ -615,12 +615,15 @@ static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_
   return launch_stamped(kern, dim3(t.N / (16 * kNT), max_tiles), dim3(kFfnThreads), lds, s, t);
 }
 
+// (the staging area of 8 rows; the reduction area and the selection's LDS are smaller)
+static size_t small_stage_bytes(int K, bool lo) { return (size_t)kSmallRowsMax * K * 2 * (lo ? 2 : 1) + (size_t)K * 2; }
+constexpr size_t kTwoPerCu = 72 * 1024;
+
 int small_tile_rows(int H, int I, bool f32_act) {
-  // (the staging area of 8 rows; the reduction area and the selection's LDS are smaller)
-  auto stage = [](int K, bool lo) { return (size_t)kSmallRowsMax * K * 2 * (lo ? 2 : 1) + (size_t)K * 2; };
-  constexpr size_t kTwoPerCu = 72 * 1024;
-  return stage(H, f32_act) <= kTwoPerCu && stage(I, true) <= kTwoPerCu ? kSmallRowsMax : 4;
+  return small_stage_bytes(H, f32_act) <= kTwoPerCu && small_stage_bytes(I, true) <= kTwoPerCu ? kSmallRowsMax : 4;
 }
+
+int small_down_tile_rows(int I) { return small_stage_bytes(I, true) <= kTwoPerCu ? kSmallRowsMax : 4; }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   hipError_t err = hipSuccess;
@@ -687,11 +690,17 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
       if (e != hipSuccess) return e;
     }
     d.tiles = a.small; d.n_tiles = a.n_small;
+    int max_dn = a.max_small;
+    if (pre && a.down_small) {   // tiles of more slots where the down projection's staging holds them
+      d.tiles = a.down_small; d.n_tiles = a.n_down_small;
+      d.stage_rows = a.T < a.bm_down_small ? a.T : a.bm_down_small;
+      max_dn = a.max_down_small;
+    }
     const FfnTileArgs& t = d;   // (the launch macros take t)
     trace_pre("ffn_down", ss, true);
     if (pre)
-      e = a.fd == FMT_Q2SM ? launch_small_t<FMT_Q2SM, 1, true, MODE_DOWN, false, false, true>(t, a.max_small, ss)
-                           : launch_small_t<FMT_Q8_0, 1, true, MODE_DOWN, false, false, true>(t, a.max_small, ss);
+      e = a.fd == FMT_Q2SM ? launch_small_t<FMT_Q2SM, 1, true, MODE_DOWN, false, false, true>(t, max_dn, ss)
+                           : launch_small_t<FMT_Q8_0, 1, true, MODE_DOWN, false, false, true>(t, max_dn, ss);
     else
       e = a.fd == FMT_Q2SM ? MOE_SMALL(FMT_Q2SM, 1, true, MODE_DOWN, ss) : MOE_SMALL(FMT_Q8_0, 1, true, MODE_DOWN, ss);
     trace_post("ffn_down", ss);

@@ -71,6 +71,10 @@ struct TileLists {
   int4* small_tok;              // tokens of the rows of each small tile: two int4 per tile (bm_small <= 8)
   const int32_t* slot_list;
   int k;
+  // non-NULL: the down projection's own small tiles, of bm_down slots (the same experts and rows)
+  int4* down;
+  int32_t* n_down;
+  int bm_down, max_down;
 };
 
 // Batches of up to kFrontMaxTokens tokens: top-k selection, grouping, tile lists and the
@@ -107,6 +111,11 @@ struct FfnArgs {
   // recorded on the second stream after them and waited for by the caller's stream)
   hipStream_t side;
   hipEvent_t fork, join;
+  // non-NULL (batches of more than kSelMaxTokens tokens where the down projection's staging holds
+  // more slots than the gate/up's): the down projection's own small tiles, of bm_down slots
+  const int4* down_small;
+  const int32_t* n_down_small;
+  int max_down_small, bm_down_small;
 };
 
 // Tile lists + fp16 activation operand (fmt.h) in one launch.
@@ -123,6 +132,8 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 constexpr int kSmallRowsMax = 8;
 constexpr int kLargeTileRows = 128;   // slots per large tile
 int small_tile_rows(int H, int I, bool f32_act);
+// Slots per small tile of the down projection alone (its staging: K = I, hi and lo planes).
+int small_down_tile_rows(int I);
 
 hipError_t launch_combine(const float* y, const float* w, const int32_t* ids, const int32_t* g2l, int T, int k,
                           int H, int E, float* out, hipStream_t s);

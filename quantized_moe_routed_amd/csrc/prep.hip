@@ -72,6 +72,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const void* __restri
                 tl.max_small, tl.small, tl.n_small, wave_tot, tl.small_tok, tl.slot_list, tl.k);
     build_tiles(tl.counts, tl.offsets, tl.g2l, tl.E, tl.E_local, tl.n_slots, tl.bm_large, tl.large_min, 0x7FFFFFFF,
                 tl.max_large, tl.large, tl.n_large, wave_tot);
+    if (tl.down)   // the down projection's small tiles: the same experts and rows, bm_down slots each
+      build_tiles(tl.counts, tl.offsets, tl.g2l, tl.E, tl.E_local, tl.n_slots, tl.bm_down, 1, tl.large_min,
+                  tl.max_down, tl.down, tl.n_down, wave_tot);
   } else {
     const int t = blockIdx.x - 1;
     if (t < T) prep_token<ACT, kPrepThreads>(x, t, H, nb32, xq_hi, xq_lo, sq_hi, sq_lo, sigma);

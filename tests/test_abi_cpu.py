@@ -192,9 +192,11 @@ def test_bf16_forward_format_limits():
     # fp32 activations add the lo plane and, their staging of 8 rows not fitting two workgroups per
     # compute unit at H = 4096, take small tiles of 4 slots.  Large tiles take every expert of 12
     # slots or more (T = 2048), so an expert has at most ceil(11 / 4) = 3 small tiles of 4 slots
-    # against ceil(11 / 8) = 2 of 8: 256 more tiles of 16 + 32 bytes
+    # against ceil(11 / 8) = 2 of 8: 256 more tiles of 16 + 32 bytes.  The down projection, whose
+    # staging of 8 rows does fit (K = I = 2048), keeps a list of its own small tiles of 8 slots: at
+    # most 2 per expert, 512 tiles of 16 bytes, and its count (one 256-byte aligned slot)
     assert moe.large_tile_min(2048) == 12
-    assert f[2] == a[2] + 2048 * 4096 * 2 + 256 * (3 - 2) * (16 + 32)
+    assert f[2] == a[2] + 2048 * 4096 * 2 + 256 * (3 - 2) * (16 + 32) + 512 * 16 + 256
 
 
 def test_build_scan_flags_dpp_operand_written_too_late():

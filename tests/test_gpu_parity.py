@@ -366,6 +366,32 @@ def test_topk_ties_against_a_stable_sort(torch, E, k):
         assert_close(got[1].reshape(T, k), np.tile(sg / sg.sum(), (T, 1)), what=f"weights E={E} k={k}")
 
 
+@pytest.mark.parametrize("cfg,T", [(3, 32), (5, 128)])
+def test_down_tiles_of_eight_beside_gateup_tiles_of_four(torch, cfg, T):
+    """fp32 activations at H = 4096: the gate/up projection takes small tiles of 4 slots (its staging
+    of 8 rows would not let two workgroups share a compute unit) while the down projection, whose
+    staging of 8 rows fits (K = I = 2048), takes tiles of its own of 8.  The y_slot rows of every
+    expert of 5 to 8 slots (two gate/up tiles, one down tile) equal the oracle's expert outputs."""
+    _say(f"down tiles of 8 beside gate/up tiles of 4: cfg{cfg} T={T}")
+    wl = synth.make(cfg, T=T)
+    g2l = l2g = None
+    if cfg == 5:
+        owner = moe.place_lpt(wl.load_hist, 2)
+        g2l, l2g = moe.share_tables(owner, 0)
+    layer = make_layer(wl, l2g=l2g, g2l=g2l)
+    got = run(layer, wl, torch)
+    counts, offsets, slots = got["counts"], got["offsets"], got["slot_list"]
+    owned = np.ones(wl.E, bool) if g2l is None else np.asarray(g2l) >= 0
+    mid = [e for e in range(wl.E) if owned[e] and 5 <= counts[e] <= 8]
+    assert mid, "no owned expert of 5 to 8 slots"
+    pick = [int(sl) for e in mid[:6] for sl in slots[offsets[e]:offsets[e + 1]]]
+    gate, up, down = (wl.gate, wl.up, wl.down) if l2g is None else (wl.gate[l2g], wl.up[l2g], wl.down[l2g])
+    rows = oracle.forward_slots(helpers.fmts(wl), gate, up, down, wl.x, got["ids"], pick,
+                                g2l=None if g2l is None else np.asarray(g2l))
+    ref = np.stack([rows[sl] for sl in pick])
+    assert_close(got["y"][pick], ref, f"cfg{cfg} y rows of experts of 5-8 slots")
+
+
 @pytest.mark.parametrize("T,k,E", [(300, 8, 256), (2049, 8, 64), (129, 8, 1024), (4096, 1, 3)])
 def test_group_over_several_chunks(torch, T, k, E):
     """The grouping launch takes 1024 slots per workgroup: batches of several chunks with a ragged
