@@ -119,13 +119,15 @@ struct TilePlan {
   int bm_down, max_down;   // max_down > 0: the down projection's own small tiles of bm_down slots
 };
 
-TilePlan tile_plan(int T, int H, int I, int k, int E_local, int xt) {
+// half: the 2-bit gate/up stages its rows one code unit at a time (moe::half_gateup_staging), which
+// lets its small tiles take 8 slots
+TilePlan tile_plan(int T, int H, int I, int k, int E_local, int xt, bool half = false) {
   const int64_t slots = (int64_t)T * k;
   TilePlan p{};
   const int lmin = large_tile_min(T);
   const bool large = lmin > 0;
   p.large_min = large ? lmin : 0x7FFFFFFF;
-  p.bm_small = moe::small_tile_rows(H, I, xt == MOE_ACT_F32);
+  p.bm_small = half ? moe::kSmallRowsMax : moe::small_tile_rows(H, I, xt == MOE_ACT_F32);
   // (one token: each of its k experts is a tile of one slot, so at most min(k, E_local) tiles; the
   // launches' grids hold exactly the tiles that can occur)
   p.max_small = T == 1 ? std::min(k, E_local) : (int)max_tiles(slots, std::min<int64_t>(E_local, slots), p.bm_small);
@@ -137,12 +139,12 @@ TilePlan tile_plan(int T, int H, int I, int k, int E_local, int xt) {
                                                           ((lmin - 1 + p.bm_small - 1) / p.bm_small));
   p.max_large = large ? (int)max_tiles(slots, std::min<int64_t>(E_local, slots / lmin), kLargeTile) : 0;
   // past kSelMaxTokens tokens the down projection stages prepared rows, and where its staging (K = I)
-  // holds more slots than the gate/up's (K = H, fp32 activations), its small tiles take that many:
-  // an expert of 5-8 slots then streams its down weights once instead of on two tiles
+  // holds another number of slots than the gate/up's (K = H, fp32 activations), its small tiles take
+  // that many: an expert of 5-8 slots then streams its down weights once instead of on two tiles
   p.bm_down = p.bm_small;
   p.max_down = 0;
   const int bmd = moe::small_down_tile_rows(I);
-  if (T > moe::kSelMaxTokens && bmd > p.bm_small) {
+  if (T > moe::kSelMaxTokens && bmd != p.bm_small) {
     p.bm_down = bmd;
     p.max_down = (int)max_tiles(slots, std::min<int64_t>(E_local, slots), bmd);
     if (large)
@@ -162,7 +164,13 @@ FwdLayout fwd_layout(int T, int H, int I, int k, int E_local, int xt) {
   FwdLayout L{};
   const size_t TK = (size_t)T * k;
   const size_t nb32H = pad32(H / 32), nb32I = pad32(I / 32);
-  const TilePlan tp = tile_plan(T, H, I, k, E_local, xt);
+  // the weight format is not known here: room for the tile lists of either gate/up staging
+  TilePlan tp = tile_plan(T, H, I, k, E_local, xt);
+  if (T > moe::kSelMaxTokens && moe::half_gateup_staging(H, xt == MOE_ACT_F32)) {
+    const TilePlan th = tile_plan(T, H, I, k, E_local, xt, true);
+    tp.max_small = std::max(tp.max_small, th.max_small);
+    tp.max_down = std::max(tp.max_down, th.max_down);
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -415,7 +423,12 @@ moe_status forward_setup(const char* fn, const void* x, int32_t xt, int32_t T, i
   auto at16 = [&](size_t o) { return reinterpret_cast<uint16_t*>(wsb + o); };
   moe::FfnArgs& a = f.a;
   a = moe::FfnArgs{};
-  const TilePlan tp = tile_plan(T, H, I, k, E_local, xt);
+  // 2-bit gate/up past kSelMaxTokens tokens: its rows staged one code unit at a time where whole
+  // rows of 8 slots would not fit (tiles of 8 slots instead of 4)
+  const bool half = T > moe::kSelMaxTokens && local->gate.fmt == MOE_W_Q2SM &&
+                    moe::half_gateup_staging(H, xt == MOE_ACT_F32);
+  const TilePlan tp = tile_plan(T, H, I, k, E_local, xt, half);
+  a.half_gateup = half;
   a.T = T; a.H = H; a.I = I; a.k = k;
   a.fg = local->gate.fmt;
   a.fd = local->down.fmt;

@@ -45,6 +45,8 @@ constexpr int kFfnThreads = 512;
 constexpr int kFfnWaves = kFfnThreads / 64;
 constexpr int kNT = 2;            // 16-column output tiles per workgroup
 constexpr int kStageRows = kSmallRowsMax;   // slots per tile at most; their activation rows are staged in LDS
+// LDS of the unit-by-unit staging: per wave one unit (UB blocks) of 8 hi rows, 8 lo rows and a zero row
+constexpr size_t half_stage_bytes(int ub) { return (size_t)kFfnWaves * (2 * kStageRows + 1) * ub * 32 * 2; }
 
 // ONE: every tile holds a single slot (one token in the batch), so only the
 // first component of each output fragment is ever needed.
@@ -67,8 +69,13 @@ __host__ __device__ constexpr size_t one_red_offset(bool sel, int stage_rows, in
 // PRE (down of several slots): the operand rows come prepared (the conversion launch wrote each row
 // of h scaled and split, with its block sums and row scale), staged as they are; without PRE each
 // wave converts its own range of the fp32 rows while staging (CONV).
-template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL, bool PRE = false>
+// HALF (2-bit gate/up of several slots with a lo plane, at most two code units per wave): each
+// wave stages one code unit of its rows at a time in a window of its own, and the second after
+// the first unit is multiplied, so that 8 slots' rows take half the LDS of staging the whole range.
+template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL, bool PRE = false, bool HALF = false>
 __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a) {
+  static_assert(!HALF || (MODE == MODE_GATEUP && !ONE && !SEL && LO && F == FMT_Q2SM && NM == 2),
+                "unit-by-unit staging: 2-bit gate/up of several slots with a lo plane");
   constexpr int UB = Codes<F>::kUnitBlocks;
   constexpr bool CONV = MODE == MODE_DOWN && !ONE && !PRE;   // down of several slots: converts fp32 h while staging
   constexpr bool BSC = MODE == MODE_DOWN && ONE;     // down of one slot: block-scaled operand planes
@@ -176,14 +183,33 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   // Each wave moves its own slice of the tile's activation rows (the values of its code units) to
   // LDS with direct loads, ahead of its codes so that they are not queued behind the weight stream;
   // no other wave reads that slice, so no barrier is needed before the main loop.
-  uint16_t* st_hi = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* st_lo = st_hi + a.stage_rows * K;
-  uint16_t* st_zero = st_lo + (LO ? a.stage_rows * K : 0);   // one row of zeros for rows without a slot
+  // (HALF: wave w's window of one code unit, WV values per row: 8 hi rows, 8 lo rows, a zero row)
+  constexpr int WV = UB * 32;
+  const int RS = HALF ? WV : K;   // row stride of the staging area
+  uint16_t* st_hi = reinterpret_cast<uint16_t*>(smem) + (HALF ? (size_t)wave * (2 * kStageRows + 1) * WV : 0);
+  uint16_t* st_lo = st_hi + (HALF ? kStageRows * WV : a.stage_rows * K);
+  uint16_t* st_zero = HALF ? st_hi + 2 * kStageRows * WV
+                           : st_lo + (LO ? a.stage_rows * K : 0);   // one row of zeros for rows without a slot
   if constexpr (MODE == MODE_GATEUP || PRE)   // the rows' scales (prepared down operand: per grouped position)
     if (tid < kStageRows) s_sig[tid] = tid < rows ? a.sigma[row_of(tid)] : 1.0f;
   const int k0 = 32 * UB * u_beg, k1 = min(32 * UB * u_end, K);
-  for (int e = k0 + 8 * lane; e < k1; e += 8 * kWave)
-    *reinterpret_cast<uint4*>(st_zero + e) = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (HALF) {
+    for (int e = 8 * lane; e < WV; e += 8 * kWave) *reinterpret_cast<uint4*>(st_zero + e) = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    for (int e = k0 + 8 * lane; e < k1; e += 8 * kWave)
+      *reinterpret_cast<uint4*>(st_zero + e) = make_uint4(0u, 0u, 0u, 0u);
+  }
+  // HALF: code unit u of the rows into this wave's window (lanes past the unit or the row load nothing)
+  [[maybe_unused]] auto stage_unit = [&](int u) {
+    const uint32_t w0 = (uint32_t)(uintptr_t)st_hi;
+    const int e = 32 * UB * u + 8 * lane;
+    for (int pl = 0; pl < 2; ++pl)
+      for (int m = 0; m < rows; ++m)
+        if (8 * lane < WV && e < K) {
+          const uint16_t* src = (pl ? a.a_lo : a.a_hi) + (int64_t)row_of(m) * K + e;
+          dma16(src, __builtin_amdgcn_readfirstlane(w0 + (uint32_t)((pl * kStageRows + m) * WV * 2)));
+        }
+  };
   // down: the fp32 h of this wave's range [k0, k1) of every row goes by direct loads into the LDS
   // bytes that its fp16 pairs will occupy: pass q (values 256 q .. 256 q + n - 1 of the range, n at
   // most 256) puts its first n / 2 values into the hi plane's bytes of the pass and the rest into
@@ -225,6 +251,8 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
     const float* pm = a.hmf + (int64_t)(p0 + (mr < rows ? mr : 0)) * a.nb32 + lane % LPR;
 #pragma unroll
     for (int j = 0; j < HMJ; ++j) hmv[j] = pm[min(LPR * j, a.nb32 - LPR)];   // (past the row: dropped below)
+  } else if constexpr (HALF) {
+    if (u_beg < u_end) stage_unit(u_beg);
   } else {   // gate/up, and one-slot down: the prepared fp16 planes as they are
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
@@ -262,7 +290,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   const int slot_m = c16 & 7;
   const bool mvalid = slot_m < rows && (c16 < 8 || LO);
   const int arow = row_of(slot_m < rows ? slot_m : 0);
-  const uint16_t* pa = (mvalid ? (c16 < 8 ? st_hi : st_lo) + slot_m * K : st_zero) + 8 * g;
+  const uint16_t* pa = (mvalid ? (c16 < 8 ? st_hi : st_lo) + slot_m * RS : st_zero) + 8 * g;
   // the m-term operand: rows 0..7 hi, 8..15 lo of the block sums
   const bool svalid = slot_m < rows;
   const uint16_t* ps = (c16 < 8 ? a.s_hi : a.s_lo) + (int64_t)arow * a.nb32;
@@ -402,11 +430,19 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
     for (int j = 0; j < CH; ++j) {
       const int u = u0 + j;
       if (u >= u_end) break;
+      if constexpr (HALF) {
+        if (j > 0) {
+          // the previous unit's operand reads are done; the next unit into the same window
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          stage_unit(u);
+          wait_vmem();
+        }
+      }
 #pragma unroll
       for (int i = 0; i < UB; ++i) {
         const int b = u * UB + i;
         if (b >= nb) break;
-        const uint4 av = *reinterpret_cast<const uint4*>(pa + 32 * b);
+        const uint4 av = *reinterpret_cast<const uint4*>(pa + 32 * (HALF ? i : b));
         // one slot: the block's inverse operand scale, folded into its weight scales
         [[maybe_unused]] float fb = 1.0f;
         if constexpr (BSC)
@@ -595,9 +631,10 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   }
 }
 
-template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL = false, bool PRE = false>
+template <int F, int NM, bool LO, int MODE, bool ONE, bool SEL = false, bool PRE = false, bool HALF = false>
 static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_t s) {
-  const size_t stage = (size_t)t.stage_rows * t.K * 2 * (LO ? 2 : 1) + (size_t)t.K * 2;
+  const size_t stage = HALF ? half_stage_bytes(Codes<F>::kUnitBlocks)
+                            : (size_t)t.stage_rows * t.K * 2 * (LO ? 2 : 1) + (size_t)t.K * 2;
   const size_t red = (size_t)kFfnWaves * kNT * NM * 4 * kWave * 4 + kStageRows * 33 * 4;
   size_t lds = stage > red ? stage : red;
   if (SEL && lds < kSelScratchBytes) lds = kSelScratchBytes;
@@ -606,7 +643,7 @@ static hipError_t launch_small_t(const FfnTileArgs& t, int max_tiles, hipStream_
     if (lds < one) lds = one;
   }
 
-  auto kern = ffn_small_kernel<F, NM, LO, MODE, ONE, SEL, PRE>;
+  auto kern = ffn_small_kernel<F, NM, LO, MODE, ONE, SEL, PRE, HALF>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -624,6 +661,12 @@ int small_tile_rows(int H, int I, bool f32_act) {
 }
 
 int small_down_tile_rows(int I) { return small_stage_bytes(I, true) <= kTwoPerCu ? kSmallRowsMax : 4; }
+
+bool half_gateup_staging(int H, bool f32_act) {
+  const int n_units = (H / 32 + Codes<FMT_Q2SM>::kUnitBlocks - 1) / Codes<FMT_Q2SM>::kUnitBlocks;
+  return f32_act && small_stage_bytes(H, true) > kTwoPerCu && n_units <= 2 * kFfnWaves &&
+         half_stage_bytes(Codes<FMT_Q2SM>::kUnitBlocks) <= kTwoPerCu;
+}
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   hipError_t err = hipSuccess;
@@ -675,7 +718,10 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
       if (a.fg == FMT_Q2SM) e = lo ? MOE_SMALL_SEL(FMT_Q2SM, true) : MOE_SMALL_SEL(FMT_Q2SM, false);
       else e = lo ? MOE_SMALL_SEL(FMT_Q8_0, true) : MOE_SMALL_SEL(FMT_Q8_0, false);
     } else if (a.fg == FMT_Q2SM) {
-      e = lo ? MOE_SMALL(FMT_Q2SM, 2, true, MODE_GATEUP, ss) : MOE_SMALL(FMT_Q2SM, 2, false, MODE_GATEUP, ss);
+      if (a.half_gateup && lo && !one)   // (tiles of 8 slots, staged unit by unit)
+        e = launch_small_t<FMT_Q2SM, 2, true, MODE_GATEUP, false, false, false, true>(t, a.max_small, ss);
+      else
+        e = lo ? MOE_SMALL(FMT_Q2SM, 2, true, MODE_GATEUP, ss) : MOE_SMALL(FMT_Q2SM, 2, false, MODE_GATEUP, ss);
     } else {
       e = lo ? MOE_SMALL(FMT_Q8_0, 2, true, MODE_GATEUP, ss) : MOE_SMALL(FMT_Q8_0, 2, false, MODE_GATEUP, ss);
     }

@@ -116,6 +116,9 @@ struct FfnArgs {
   const int4* down_small;
   const int32_t* n_down_small;
   int max_down_small, bm_down_small;
+  // the 2-bit gate/up of several slots stages its rows one code unit at a time (tiles of 8 slots
+  // where staging whole rows would take 4)
+  bool half_gateup;
 };
 
 // Tile lists + fp16 activation operand (fmt.h) in one launch.
@@ -134,6 +137,10 @@ constexpr int kLargeTileRows = 128;   // slots per large tile
 int small_tile_rows(int H, int I, bool f32_act);
 // Slots per small tile of the down projection alone (its staging: K = I, hi and lo planes).
 int small_down_tile_rows(int I);
+// Whether the 2-bit gate/up of several slots (batches past kSelMaxTokens tokens, fp32 activations)
+// stages its rows one code unit at a time: where 8 whole rows would not let two workgroups share a
+// compute unit and a wave takes at most two code units (K = H <= 4096).
+bool half_gateup_staging(int H, bool f32_act);
 
 hipError_t launch_combine(const float* y, const float* w, const int32_t* ids, const int32_t* g2l, int T, int k,
                           int H, int E, float* out, hipStream_t s);
