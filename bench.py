@@ -358,9 +358,9 @@ _FFN_SOURCES = ["quantized_moe_routed_amd/csrc/ffn.hip", "quantized_moe_routed_a
                 "quantized_moe_routed_amd/csrc/smallsel.h", "quantized_moe_routed_amd/csrc/select.h",
                 "quantized_moe_routed_amd/csrc/launch.h"]
 TRAFFIC_KERNELS = {
-    "decode": ("ffn_gateup", "moe::ffn_small_kernel<2, 2, true, 0, true, true, false>", _FFN_SOURCES),
-    "batched_decode": ("ffn_gateup", "moe::ffn_small_kernel<2, 2, true, 0, false, false, false>", _FFN_SOURCES),
-    "ep_share": ("ffn_gateup", "moe::ffn_small_kernel<2, 2, true, 0, false, false, false>", _FFN_SOURCES),
+    "decode": ("ffn_gateup", "moe::ffn_small_kernel<2, 2, true, 0, true, true, false, false>", _FFN_SOURCES),
+    "batched_decode": ("ffn_gateup", "moe::ffn_small_kernel<2, 2, true, 0, false, false, false, true>", _FFN_SOURCES),
+    "ep_share": ("ffn_gateup", "moe::ffn_small_kernel<2, 2, true, 0, false, false, false, true>", _FFN_SOURCES),
     "prefill": ("ffn_gateup_large", "moe::ffn_large_kernel<2, 2, false, 0, 1, 2, 4>",
                 ["quantized_moe_routed_amd/csrc/ffn_large.hip", "quantized_moe_routed_amd/csrc/ffn.h",
                  "quantized_moe_routed_amd/csrc/fmt.h", "quantized_moe_routed_amd/csrc/device.h",
