@@ -186,12 +186,22 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
   // (HALF: wave w's window of one code unit, WV values per row: 8 hi rows, 8 lo rows, a zero row)
   constexpr int WV = UB * 32;
   const int RS = HALF ? WV : K;   // row stride of the staging area
+  // (the staging loops' fields, kept in registers: the staging loads are inline assembly with a
+  // memory clobber, after which a field read through the argument block would be loaded again,
+  // a scalar load and its wait before every staging load)
+  const uint16_t* const ahi = a.a_hi;
+  const uint16_t* const alo = a.a_lo;
+  [[maybe_unused]] const float* const hf = a.hf;
+  const int srows = a.stage_rows;
   uint16_t* st_hi = reinterpret_cast<uint16_t*>(smem) + (HALF ? (size_t)wave * (2 * kStageRows + 1) * WV : 0);
-  uint16_t* st_lo = st_hi + (HALF ? kStageRows * WV : a.stage_rows * K);
+  uint16_t* st_lo = st_hi + (HALF ? kStageRows * WV : srows * K);
   uint16_t* st_zero = HALF ? st_hi + 2 * kStageRows * WV
-                           : st_lo + (LO ? a.stage_rows * K : 0);   // one row of zeros for rows without a slot
-  if constexpr (MODE == MODE_GATEUP || PRE)   // the rows' scales (prepared down operand: per grouped position)
-    if (tid < kStageRows) s_sig[tid] = tid < rows ? a.sigma[row_of(tid)] : 1.0f;
+                           : st_lo + (LO ? srows * K : 0);   // one row of zeros for rows without a slot
+  // the rows' scales (prepared down operand: per grouped position), loaded now and stored in LDS
+  // after the main loop, so that no wait for them holds back the loads below
+  [[maybe_unused]] float sig_row = 1.0f;
+  if constexpr (MODE == MODE_GATEUP || PRE)
+    if (tid < kStageRows && tid < rows) sig_row = a.sigma[row_of(tid)];
   const int k0 = 32 * UB * u_beg, k1 = min(32 * UB * u_end, K);
   if constexpr (HALF) {
     for (int e = 8 * lane; e < WV; e += 8 * kWave) *reinterpret_cast<uint4*>(st_zero + e) = make_uint4(0u, 0u, 0u, 0u);
@@ -200,15 +210,18 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
       *reinterpret_cast<uint4*>(st_zero + e) = make_uint4(0u, 0u, 0u, 0u);
   }
   // HALF: code unit u of the rows into this wave's window (lanes past the unit or the row load nothing)
-  [[maybe_unused]] auto stage_unit = [&](int u) {
+  [[maybe_unused]] auto stage_unit = [&, ahi, alo](int u) {
     const uint32_t w0 = (uint32_t)(uintptr_t)st_hi;
     const int e = 32 * UB * u + 8 * lane;
-    for (int pl = 0; pl < 2; ++pl)
-      for (int m = 0; m < rows; ++m)
-        if (8 * lane < WV && e < K) {
-          const uint16_t* src = (pl ? a.a_lo : a.a_hi) + (int64_t)row_of(m) * K + e;
-          dma16(src, __builtin_amdgcn_readfirstlane(w0 + (uint32_t)((pl * kStageRows + m) * WV * 2)));
-        }
+    if (8 * lane < WV && e < K) {
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) {
+        const uint16_t* base = (pl ? alo : ahi) + e;
+        for (int m = 0; m < rows; ++m)
+          dma16(base + (int64_t)row_of(m) * K,
+                __builtin_amdgcn_readfirstlane(w0 + (uint32_t)((pl * kStageRows + m) * WV * 2)));
+      }
+    }
   };
   // down: the fp32 h of this wave's range [k0, k1) of every row goes by direct loads into the LDS
   // bytes that its fp16 pairs will occupy: pass q (values 256 q .. 256 q + n - 1 of the range, n at
@@ -242,8 +255,8 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
         const int hq = min(4 * kWave, k1 - k0 - q0) / 2;   // values of the pass in each plane
         if (4 * lane < hq)
           for (int pl = 0; pl < 2; ++pl) {
-            const float* src = a.hf + (int64_t)(p0 + m) * K + k0 + q0 + pl * hq + 4 * lane;
-            const uint32_t dst = lds0 + (uint32_t)((((pl ? a.stage_rows : 0) + m) * K + k0 + q0) * 2);
+            const float* src = hf + (int64_t)(p0 + m) * K + k0 + q0 + pl * hq + 4 * lane;
+            const uint32_t dst = lds0 + (uint32_t)((((pl ? srows : 0) + m) * K + k0 + q0) * 2);
             dma16(src, __builtin_amdgcn_readfirstlane(dst));
           }
       }
@@ -261,8 +274,8 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
         for (int c0 = k0; c0 < k1; c0 += 512) {   // 1 KiB per instruction
           const int e = c0 + 8 * lane;
           if (e < k1) {
-            const uint16_t* src = (pl ? a.a_lo : a.a_hi) + (int64_t)(BSC ? p0 + m : row_of(m)) * K + e;
-            const uint32_t dst = lds0 + (uint32_t)((((pl ? a.stage_rows : 0) + m) * K + c0) * 2);
+            const uint16_t* src = (pl ? alo : ahi) + (int64_t)(BSC ? p0 + m : row_of(m)) * K + e;
+            const uint32_t dst = lds0 + (uint32_t)((((pl ? srows : 0) + m) * K + c0) * 2);
             dma16(src, __builtin_amdgcn_readfirstlane(dst));
           }
         }
@@ -475,6 +488,8 @@ __global__ __launch_bounds__(kFfnThreads, 4) void ffn_small_kernel(FfnTileArgs a
       }
     }
   }
+  if constexpr (MODE == MODE_GATEUP || PRE)
+    if (tid < kStageRows) s_sig[tid] = sig_row;   // (read after the reduction's barrier)
   // m-term of the remaining groups (more than 4 units per wave)
   if constexpr (Codes<F>::kHasM) {
     for (int ug = u_beg + 4; ug < u_end; ug += 4) {
