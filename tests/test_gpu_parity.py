@@ -587,3 +587,19 @@ def test_shared_expert_adds_to_the_routed_output(torch, T, act, sfmt):
     torch.cuda.synchronize()
     ref = oracle_expect(wl)["out"].astype(np.float64) + oracle.shared_expert((sfmt,) * 3, sg, su, sd, wl.x)
     assert_close(b.out.cpu().numpy(), ref, f"shared {act} T={T} out")
+
+
+@pytest.mark.parametrize("T,H", [(24, 3104), (20, 2304)])
+def test_unit_by_unit_gateup_odd_widths(torch, T, H):
+    """2-bit gate/up of several slots with fp32 activations where the whole staging of 8 rows would
+    not let two workgroups share a compute unit, so each wave stages its rows a code unit at a
+    time: H = 3104 (97 blocks: 13 units, the last of one block; waves of two, one or no units) and
+    H = 2304 (9 whole units: waves of two units, of one, and without), with tiles of up to 8 slots
+    (zipf routing gives some experts more than 8)."""
+    _say(f"unit-by-unit gate/up: T={T} H={H}")
+    assert moe.large_tile_min(T) == 0
+    wl = synth.make(synth.custom(T, H, 16, 128, 4, gate_fmt=2, up_fmt=2, down_fmt=1, router_fmt=1, act="f32",
+                                 bias="zipf1.1", name=f"unitwise_{H}"))
+    got = run(make_layer(wl), wl, torch)
+    assert got["counts"].max() > 8
+    check_against_oracle(wl, got, oracle_expect(wl), what=f"unit-by-unit H={H}")
